@@ -1,0 +1,173 @@
+"""CPU oracle for dense descriptor matching (fp64, plain loops, OpenMP over queries).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The HIP library and
+its binding never do, and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (built into ``liboracle.so`` next to it);
+this module only marshals numpy arrays. What each function computes, and the
+passages of the pages it follows, is documented in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, F16, BF16 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (IEEE double semantics: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    """Open a compiled oracle library and declare its C signatures."""
+    lib = C.CDLL(path)
+    P = C.c_void_p
+    i64, i32, dbl = C.c_int64, C.c_int, C.c_double
+    lib.orc_decode.argtypes = [P, i32, i64, P]
+    lib.orc_decode.restype = i32
+    lib.orc_nn.argtypes = [P, P, i64, P, i64, i32, P, P, P]
+    lib.orc_nn.restype = None
+    lib.orc_seed_grid.argtypes = [i32, i32, i32, P]
+    lib.orc_seed_grid.restype = i64
+    lib.orc_frm.argtypes = [P, i64, P, i64, i32, P, i64, i32, dbl, P, P, P, P, P, P, P, P]
+    lib.orc_frm.restype = i32
+    lib.orc_merge.argtypes = [P, P, P, P, i64, P, P, P]
+    lib.orc_merge.restype = i64
+    lib.orc_mutual.argtypes = [P, i64, P, i64, i32, P, P, P, P, P, P, P, P, P]
+    lib.orc_mutual.restype = i64
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+class use_library:
+    """Context manager: route every oracle call through another build of oracle.c
+    (the mutation tests use it to check that the pins catch planted mistakes)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = _lib
+        _lib = _bind(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def decode(stored: np.ndarray, dtype: int) -> np.ndarray:
+    """Stored float32 / float16 / bfloat16-bits array -> float64 array of the same shape."""
+    lib = _load()
+    src = np.ascontiguousarray(stored)
+    want = {F32: np.float32, F16: np.float16, BF16: np.uint16}[dtype]
+    if src.dtype != want:
+        raise TypeError(f"stored dtype {src.dtype} does not match code {dtype}")
+    out = np.empty(src.shape, dtype=np.float64)
+    if lib.orc_decode(_p(src), dtype, src.size, _p(out)) != 0:
+        raise ValueError("bad dtype")
+    return out
+
+
+def _rows(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    return x.reshape(-1, x.shape[-1])
+
+
+def nn(Q: np.ndarray, R: np.ndarray, qrows=None):
+    """Brute-force NN of rows of Q (or of Q[qrows]) over all rows of R.
+
+    Returns (idx int32, s1 float64, margin float64)."""
+    lib = _load()
+    Q, R = _rows(Q), _rows(R)
+    d = Q.shape[1]
+    if qrows is not None:
+        qrows = np.ascontiguousarray(qrows, dtype=np.int32)
+        nq = qrows.size
+    else:
+        nq = Q.shape[0]
+    idx = np.empty(nq, np.int32)
+    s1 = np.empty(nq, np.float64)
+    s2 = np.empty(nq, np.float64)
+    lib.orc_nn(_p(Q), _p(qrows) if qrows is not None else None, nq, _p(R), R.shape[0], d,
+               _p(idx), _p(s1), _p(s2))
+    return idx, s1, s1 - s2
+
+
+def seed_grid(H: int, W: int, S: int) -> np.ndarray:
+    lib = _load()
+    k = lib.orc_seed_grid(H, W, S, None)
+    out = np.empty(max(k, 0), np.int32)
+    lib.orc_seed_grid(H, W, S, _p(out) if k > 0 else None)
+    return out
+
+
+def frm(D1: np.ndarray, D2: np.ndarray, seeds: np.ndarray, max_iter: int, tau: float = 1e-4):
+    """FRM from the given image-1 seeds. D1, D2: float64 [N, d] or [H, W, d].
+
+    Returns a dict: per-seed u, v, score, conv_iter, active, ambiguous; the merged
+    unique pairs i, j, s (ascending i); niter; n_fwd / n_bwd = queries per iteration."""
+    lib = _load()
+    A, B = _rows(D1), _rows(D2)
+    seeds = np.ascontiguousarray(seeds, dtype=np.int32)
+    k = seeds.size
+    u = np.empty(k, np.int32); v = np.empty(k, np.int32)
+    score = np.empty(k, np.float64); conv = np.empty(k, np.int32)
+    active = np.empty(k, np.uint8); amb = np.empty(k, np.uint8)
+    nf = np.zeros(max(max_iter, 1), np.int64); nb = np.zeros(max(max_iter, 1), np.int64)
+    niter = lib.orc_frm(_p(A), A.shape[0], _p(B), B.shape[0], A.shape[1], _p(seeds), k, max_iter, tau,
+                        _p(u), _p(v), _p(score), _p(conv), _p(active), _p(amb), _p(nf), _p(nb))
+    if niter < 0:
+        raise MemoryError
+    oi = np.empty(k, np.int32); oj = np.empty(k, np.int32); os_ = np.empty(k, np.float64)
+    n = lib.orc_merge(_p(u), _p(v), _p(score), _p(active), k, _p(oi), _p(oj), _p(os_))
+    return dict(u=u, v=v, score=score, conv_iter=conv, active=active.astype(bool),
+                ambiguous=amb.astype(bool), i=oi[:n].copy(), j=oj[:n].copy(), s=os_[:n].copy(),
+                niter=int(niter), n_fwd=nf[:max_iter], n_bwd=nb[:max_iter])
+
+
+def mutual(D1: np.ndarray, D2: np.ndarray):
+    """Exhaustive mutual NN. Returns dict with pairs i, j, s and both NN tables with margins."""
+    lib = _load()
+    A, B = _rows(D1), _rows(D2)
+    N1, N2, d = A.shape[0], B.shape[0], A.shape[1]
+    nn12 = np.empty(N1, np.int32); s12 = np.empty(N1); m12 = np.empty(N1)
+    nn21 = np.empty(N2, np.int32); s21 = np.empty(N2); m21 = np.empty(N2)
+    oi = np.empty(min(N1, N2), np.int32); oj = np.empty(min(N1, N2), np.int32); os_ = np.empty(min(N1, N2))
+    n = lib.orc_mutual(_p(A), N1, _p(B), N2, d, _p(nn12), _p(s12), _p(m12), _p(nn21), _p(s21), _p(m21),
+                       _p(oi), _p(oj), _p(os_))
+    if n < 0:
+        raise MemoryError
+    return dict(i=oi[:n].copy(), j=oj[:n].copy(), s=os_[:n].copy(), nn12=nn12, s12=s12, m12=m12,
+                nn21=nn21, s21=s21, m21=m21)

@@ -1,0 +1,99 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutation edits one spot of a private copy of oracle/oracle.c (a dropped
+term, a flipped comparison, a wrong index, a swapped operand, an off-by-one),
+builds it with gcc into a temporary directory and runs the pins of
+test_oracle_pins.py against that build. At least one pin must fail for every
+mutation; the unmodified source must pass them all.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTATIONS = {
+    "dropped_first_term": ("for (int c = 0; c < d; ++c) s += a[c] * b[c];",
+                           "for (int c = 1; c < d; ++c) s += a[c] * b[c];"),
+    "dropped_last_term": ("for (int c = 0; c < d; ++c) s += a[c] * b[c];",
+                          "for (int c = 0; c + 1 < d; ++c) s += a[c] * b[c];"),
+    "wrong_sign": ("s += a[c] * b[c];", "s -= a[c] * b[c];"),
+    "ties_to_highest": ("if (s > b1) { b2 = b1;", "if (s >= b1) { b2 = b1;"),
+    "no_second_best": ("else if (s > b2) { b2 = s; }", "else if (s > b1) { b2 = s; }"),
+    "half_exponent_bias": ("v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 24);"),
+    "half_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "seed_offset_zero": ("for (int y = S / 2; y < H; y += S)", "for (int y = 0; y < H; y += S)"),
+    "seed_index_transposed": ("if (out) out[k] = x + W * y;", "if (out) out[k] = y + H * x;"),
+    "forward_test_vs_u": ("if (active[a] && v[a] == v_old[a])", "if (active[a] && v[a] == u_old[a])"),
+    "backward_test_vs_v": ("if (active[a] && u[a] == u_old[a])", "if (active[a] && u[a] == v_old[a])"),
+    "no_forward_test": ("if (active[a] && v[a] == v_old[a])", "if (0 && v[a] == v_old[a])"),
+    "max_iter_off_by_one": ("if (niter >= max_iter) break;", "if (niter > max_iter) break;"),
+    "old_not_updated": ("for (int64_t a = 0; a < k; ++a) { v_old[a] = v[a]; u_old[a] = u[a]; }",
+                        "for (int64_t a = 0; a < k; ++a) { v_old[a] = v[a]; }"),
+    "backward_against_own_map": ("nn_one(D2 + (int64_t)v[a] * d, D1, N1, d, &i, &s1, &s2);",
+                                 "nn_one(D2 + (int64_t)v[a] * d, D2, N2, d, &i, &s1, &s2);"),
+    "forward_query_from_wrong_map": ("nn_one(D1 + (int64_t)u[a] * d, D2, N2, d, &j, &s1, &s2);",
+                                     "nn_one(D2 + (int64_t)u[a] * d, D2, N2, d, &j, &s1, &s2);"),
+    "converged_keeps_active": ("if (active[a]) continue;\n        buf[3 * m]", "if (!active[a]) continue;\n        buf[3 * m]"),
+    "mutual_check_wrong_table": ("if (nn21[j] == (int32_t)i) {", "if (nn12[j] == (int32_t)i) {"),
+    "mutual_score_wrong": ("out_s[n] = s12[i];", "out_s[n] = s21[i];"),
+}
+
+# pins, as callables with fixed arguments
+PINS = [
+    P.test_decode_f16_all_patterns,
+    lambda: P.test_nn_matches_numpy_argmax(37, 53, 24, 1),
+    lambda: P.test_nn_matches_numpy_argmax(5, 9, 1, 3),
+    P.test_nn_ties_take_lowest_index,
+    P.test_nn_score_is_exact_for_f16_inputs,
+    P.test_seed_grid_closed_forms,
+    lambda: P.test_frm_handworked_fixture("row"),
+    lambda: P.test_frm_equals_orbit_derivation((12, 9), (12, 9), 24, 23, 10),
+    lambda: P.test_frm_equals_orbit_derivation((6, 10), (9, 7), 2, 22, 2),
+    lambda: P.test_frm_pairs_are_reciprocal_and_inside_mutual_set(31),
+    P.test_frm_identity_map,
+    lambda: P.test_frm_pure_shift_closed_form(3, 2),
+    lambda: P.test_mutual_matches_numpy((7, 9), (11, 5), 3, 52),
+    P.test_mutual_symmetry,
+]
+
+
+def _build(src_text, out_dir, name):
+    c_path = os.path.join(out_dir, f"{name}.c")
+    so_path = os.path.join(out_dir, f"{name}.so")
+    with open(c_path, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", so_path, c_path, "-lm"], check=True)
+    return so_path
+
+
+def _failures(so_path):
+    failed = 0
+    with oracle.use_library(so_path):
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, IndexError, ValueError, MemoryError):
+                failed += 1
+    return failed
+
+
+def test_unmodified_source_passes_all_pins(tmp_path):
+    with open(SRC) as f:
+        text = f.read()
+    assert _failures(_build(text, str(tmp_path), "orig")) == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    with open(SRC) as f:
+        text = f.read()
+    old, new = MUTATIONS[name]
+    assert text.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = text.replace(old, new, 1)
+    assert _failures(_build(mutated, str(tmp_path), name)) >= 1, f"no pin caught mutation {name}"
