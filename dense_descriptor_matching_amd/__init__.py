@@ -1,0 +1,258 @@
+"""MI355X-native dense descriptor matching: Fast Reciprocal Matching and mutual NN.
+
+Thin ctypes binding over the C ABI of ``libddm.so`` (declared in
+``include/ddm.h``). It only marshals arguments: torch supplies device memory and
+the current HIP stream, every step of the computation runs in the library's
+HIP kernels. There is no CPU fallback: if the library is missing the calls
+raise.
+
+Matching follows MASt3R: unit-norm descriptor maps D1, D2 of shape [H, W, d];
+NN = arg-max of the dot product; the reciprocal set M = {(i, j) : j = NN2(i),
+i = NN1(j)}; Fast Reciprocal Matching iterates NN round trips from a regular
+seed grid and keeps the seeds that cycle ("MASt3R" note on cv-learn.com,
+section 手法とアーキテクチャ, FRM paragraph; the fast_reciprocal_NNs routine
+quoted in "DUSt3R和MASt3R论文阅读", section MASt3R matching).
+Pixel indices are linear, p = x + W * y; :func:`to_xy` converts.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libddm.so")
+
+DDM_F32, DDM_F16, DDM_BF16 = 0, 1, 2
+_DT = {torch.float32: DDM_F32, torch.float16: DDM_F16, torch.bfloat16: DDM_BF16}
+STATUS = {0: "ok", -1: "invalid argument", -2: "output capacity too small",
+          -3: "workspace missing or too small", -4: "unsupported dtype or descriptor dimension",
+          -5: "HIP error while enqueueing"}
+
+_lib = None
+
+
+class DDMError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+def _declare(lib):
+    P, I, I64, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+    lib.ddm_status_str.argtypes = [I]; lib.ddm_status_str.restype = C.c_char_p
+    lib.ddm_seed_count.argtypes = [I, I, I]; lib.ddm_seed_count.restype = I64
+    lib.ddm_nn_workspace_bytes.argtypes = [I, I, I, I, I]; lib.ddm_nn_workspace_bytes.restype = SZ
+    lib.ddm_nn.argtypes = [P, I, P, I, P, I, I, I, P, P, P, SZ, P]; lib.ddm_nn.restype = I
+    lib.ddm_frm_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]; lib.ddm_frm_workspace_bytes.restype = SZ
+    lib.ddm_frm_match.argtypes = [P, I, I, P, I, I, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
+    lib.ddm_frm_match.restype = I
+    lib.ddm_frm_match_batched.argtypes = [I, P, I, I, P, I, I, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
+    lib.ddm_frm_match_batched.restype = I
+    lib.ddm_mutual_workspace_bytes.argtypes = [I, I, I, I, I, I]; lib.ddm_mutual_workspace_bytes.restype = SZ
+    lib.ddm_mutual_nn.argtypes = [P, I, I, P, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
+    lib.ddm_mutual_nn.restype = I
+    return lib
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
+                               "(python -m dense_descriptor_matching_amd.build)")
+        _lib = _declare(C.CDLL(LIB_PATH))
+    return _lib
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_map(D, name):
+    if not isinstance(D, torch.Tensor) or not D.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if D.dtype not in _DT:
+        raise TypeError(f"{name}: unsupported dtype {D.dtype}")
+    if not D.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _rc(status, what):
+    if status != 0:
+        raise DDMError(status, what)
+
+
+def seed_count(H: int, W: int, grid_stride: int) -> int:
+    return int(lib().ddm_seed_count(H, W, grid_stride))
+
+
+def to_xy(idx: torch.Tensor, W: int):
+    """Linear pixel index -> (x, y)."""
+    return idx % W, torch.div(idx, W, rounding_mode="floor")
+
+
+# ------------------------------------------------------------------- NN
+def nn(Q: torch.Tensor, R: torch.Tensor, q_rows: torch.Tensor | None = None):
+    """Nearest neighbour of rows of Q (or Q[q_rows]) among all rows of R.
+
+    Q: [NQ, d] (or [..., d]), R: [N, d]. Returns (idx int32 [M], score float32 [M])."""
+    _check_map(Q, "Q"); _check_map(R, "R")
+    d = Q.shape[-1]
+    if R.shape[-1] != d or Q.dtype != R.dtype:
+        raise ValueError("Q and R must share d and dtype")
+    NQ, N = Q.numel() // d, R.numel() // d
+    if q_rows is not None:
+        q_rows = q_rows.to(device=Q.device, dtype=torch.int32).contiguous()
+        M = q_rows.numel()
+    else:
+        M = NQ
+    out_idx = torch.empty(M, dtype=torch.int32, device=Q.device)
+    out_s = torch.empty(M, dtype=torch.float32, device=Q.device)
+    L = lib()
+    ws = _workspace(L.ddm_nn_workspace_bytes(NQ, M, N, d, _DT[Q.dtype]), Q.device)
+    _rc(L.ddm_nn(_ptr(Q), NQ, _ptr(q_rows), M, _ptr(R), N, d, _DT[Q.dtype], _ptr(out_idx), _ptr(out_s),
+                 _ptr(ws), ws.numel(), _stream()), "ddm_nn")
+    return out_idx, out_s
+
+
+# ------------------------------------------------------------------- FRM
+class FrmBuffers:
+    """Preallocated outputs + workspace for repeated FRM calls on one shape."""
+
+    def __init__(self, B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, device, with_state=True):
+        L = lib()
+        self.k = seed_count(H1, W1, grid_stride)
+        self.cap = max(self.k, 1)
+        dev = device
+        self.out_i = torch.empty(B * self.cap, dtype=torch.int32, device=dev)
+        self.out_j = torch.empty(B * self.cap, dtype=torch.int32, device=dev)
+        self.out_s = torch.empty(B * self.cap, dtype=torch.float32, device=dev)
+        self.count = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.state = torch.empty(B * self.cap * 4, dtype=torch.int32, device=dev) if with_state else None
+        self.qcounts = torch.zeros(B * 2 * max_iter, dtype=torch.int32, device=dev)
+        nbytes = L.ddm_frm_workspace_bytes(B, H1, W1, H2, W2, d, _DT[dtype], grid_stride, max_iter)
+        if nbytes == 0:
+            raise DDMError(-1, "ddm_frm_workspace_bytes")
+        self.ws = _workspace(nbytes, dev)
+
+
+def frm_match_into(D1, D2, grid_stride, max_iter, buf: FrmBuffers, batched: bool = False):
+    """Enqueue FRM into preallocated buffers (no host synchronisation)."""
+    _check_map(D1, "D1"); _check_map(D2, "D2")
+    if D1.dtype != D2.dtype or D1.shape[-1] != D2.shape[-1]:
+        raise ValueError("D1 and D2 must share dtype and d")
+    L = lib()
+    dt = _DT[D1.dtype]
+    if batched:
+        B, H1, W1, d = D1.shape
+        B2, H2, W2, _ = D2.shape
+        if B2 != B:
+            raise ValueError("batch sizes differ")
+        _rc(L.ddm_frm_match_batched(B, _ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride, max_iter,
+                                    _ptr(buf.out_i), _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count),
+                                    _ptr(buf.state), _ptr(buf.qcounts), _ptr(buf.ws), buf.ws.numel(), _stream()),
+            "ddm_frm_match_batched")
+    else:
+        H1, W1, d = D1.shape
+        H2, W2, _ = D2.shape
+        _rc(L.ddm_frm_match(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride, max_iter,
+                            _ptr(buf.out_i), _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count),
+                            _ptr(buf.state), _ptr(buf.qcounts), _ptr(buf.ws), buf.ws.numel(), _stream()),
+            "ddm_frm_match")
+
+
+def frm_match(D1: torch.Tensor, D2: torch.Tensor, grid_stride: int = 8, max_iter: int = 10,
+              return_state: bool = False):
+    """Fast Reciprocal Matching of [H1, W1, d] and [H2, W2, d] maps.
+
+    Returns (i, j, score): converged reciprocal pairs, unique, ascending in i.
+    With return_state, also a dict with per-seed (u, v, conv_iter) [k, 3] and the
+    forward/backward query counts per iteration [2 * max_iter]."""
+    H1, W1, d = D1.shape
+    H2, W2, _ = D2.shape
+    buf = FrmBuffers(1, H1, W1, H2, W2, d, D1.dtype, grid_stride, max_iter, D1.device, with_state=return_state)
+    frm_match_into(D1, D2, grid_stride, max_iter, buf)
+    n = int(buf.count[0].item())
+    res = (buf.out_i[:n].clone(), buf.out_j[:n].clone(), buf.out_s[:n].clone())
+    if not return_state:
+        return res
+    st = buf.state.view(-1, 4)[:buf.k, :3].clone()
+    return res + (dict(state=st, query_counts=buf.qcounts.clone()),)
+
+
+def frm_match_batched(D1: torch.Tensor, D2: torch.Tensor, grid_stride: int = 8, max_iter: int = 10,
+                      return_state: bool = False):
+    """B independent pairs: D1 [B, H1, W1, d], D2 [B, H2, W2, d]. Returns a list of (i, j, score)."""
+    B, H1, W1, d = D1.shape
+    _, H2, W2, _ = D2.shape
+    buf = FrmBuffers(B, H1, W1, H2, W2, d, D1.dtype, grid_stride, max_iter, D1.device, with_state=return_state)
+    frm_match_into(D1, D2, grid_stride, max_iter, buf, batched=True)
+    counts = buf.count.cpu().tolist()
+    out = []
+    for b in range(B):
+        o = b * buf.cap
+        n = counts[b]
+        item = (buf.out_i[o:o + n].clone(), buf.out_j[o:o + n].clone(), buf.out_s[o:o + n].clone())
+        if return_state:
+            st = buf.state.view(B, buf.cap, 4)[b, :buf.k, :3].clone()
+            qc = buf.qcounts.view(B, -1)[b].clone()
+            item = item + (dict(state=st, query_counts=qc),)
+        out.append(item)
+    return out
+
+
+# ------------------------------------------------------------------- mutual NN
+class MutualBuffers:
+    def __init__(self, H1, W1, H2, W2, d, dtype, device, with_nn=False):
+        L = lib()
+        self.cap = min(H1 * W1, H2 * W2)
+        self.out_i = torch.empty(self.cap, dtype=torch.int32, device=device)
+        self.out_j = torch.empty(self.cap, dtype=torch.int32, device=device)
+        self.out_s = torch.empty(self.cap, dtype=torch.float32, device=device)
+        self.count = torch.zeros(1, dtype=torch.int32, device=device)
+        self.nn12 = torch.empty(H1 * W1, dtype=torch.int32, device=device) if with_nn else None
+        self.s12 = torch.empty(H1 * W1, dtype=torch.float32, device=device) if with_nn else None
+        nbytes = L.ddm_mutual_workspace_bytes(H1, W1, H2, W2, d, _DT[dtype])
+        if nbytes == 0:
+            raise DDMError(-1, "ddm_mutual_workspace_bytes")
+        self.ws = _workspace(nbytes, device)
+
+
+def mutual_nn_into(D1, D2, buf: MutualBuffers):
+    _check_map(D1, "D1"); _check_map(D2, "D2")
+    if D1.dtype != D2.dtype or D1.shape[-1] != D2.shape[-1]:
+        raise ValueError("D1 and D2 must share dtype and d")
+    H1, W1, d = D1.shape
+    H2, W2, _ = D2.shape
+    _rc(lib().ddm_mutual_nn(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, _DT[D1.dtype], _ptr(buf.out_i), _ptr(buf.out_j),
+                            _ptr(buf.out_s), buf.cap, _ptr(buf.count), _ptr(buf.nn12), _ptr(buf.s12), _ptr(buf.ws),
+                            buf.ws.numel(), _stream()), "ddm_mutual_nn")
+
+
+def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False):
+    """Exhaustive reciprocal nearest neighbours. Returns (i, j, score) ascending in i
+    (and, with return_nn, NN2 index and score of every pixel of image 1)."""
+    H1, W1, d = D1.shape
+    H2, W2, _ = D2.shape
+    buf = MutualBuffers(H1, W1, H2, W2, d, D1.dtype, D1.device, with_nn=return_nn)
+    mutual_nn_into(D1, D2, buf)
+    n = int(buf.count[0].item())
+    res = (buf.out_i[:n].clone(), buf.out_j[:n].clone(), buf.out_s[:n].clone())
+    if return_nn:
+        return res + (buf.nn12, buf.s12)
+    return res
+
+
+__all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "mutual_nn", "mutual_nn_into", "seed_count",
+           "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH"]

@@ -1,0 +1,496 @@
+// ddm.hip -- host side of the C ABI declared in include/ddm.h: argument
+// validation, workspace layout and the stream-ordered launch sequences.
+// Every step of every call runs in the kernels of ddm_sweep.hpp / ddm_aux.hpp;
+// the host only checks arguments and enqueues.
+#include "../../include/ddm.h"
+#include "ddm_aux.hpp"
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+using namespace ddm;
+
+namespace {
+
+// Default sweep shape: 4 waves x 8 query tiles = 512 query rows per sub-block.
+constexpr int RQ = 8;
+constexpr int NW = 4;
+constexpr int SB_ROWS = NW * RQ * 16;
+// fp32 maps: fewer query tiles so that up to 32 K-blocks of A fit in VGPRs.
+constexpr int RQ32 = 2;
+constexpr int SB_ROWS32 = NW * RQ32 * 16;
+constexpr size_t LDS_MAX = 160 * 1024;
+constexpr int MAX_PIX = 1 << 27;
+
+struct MapFmt {
+    int dtype, d;
+    int ld;        // stored row stride (elements) seen by the kernels
+    int np;        // compile-time pieces per row (0 = runtime, fp32)
+    int nkb;       // compile-time K blocks
+    int esz;       // bytes per element
+    bool repack;   // rows are copied into a zero-padded [n][ld] buffer first
+    int tile_bytes() const { return dtype == DT_F32 ? ld * 16 * 4 : np * 16 * 16; }
+    int sb_rows() const { return dtype == DT_F32 ? SB_ROWS32 : SB_ROWS; }
+};
+
+bool make_fmt(int dtype, int d, MapFmt *f) {
+    if (d < 1 || d > DDM_MAX_D) return false;
+    f->dtype = dtype; f->d = d;
+    if (dtype == DT_F32) {
+        f->ld = d; f->np = 0; f->nkb = d <= 32 ? 8 : 32; f->esz = 4; f->repack = false;
+        return true;
+    }
+    if (dtype != DT_F16 && dtype != DT_BF16) return false;
+    static const int supported[] = {1, 2, 3, 4, 6, 8, 12, 16};
+    const int need = (d + 7) / 8;
+    int np = 16;
+    for (int s : supported) if (s >= need) { np = s; break; }
+    f->np = np; f->nkb = (np + 3) / 4; f->ld = np * 8; f->esz = 2; f->repack = (f->ld != d);
+    return true;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Bump {
+    size_t off = 0;
+    size_t take(size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; }
+};
+
+int chunk_limit(const MapFmt &f, bool colmax) {
+    const size_t per_ref = (size_t)f.tile_bytes() / TILE + (colmax ? 4 : 0);
+    int c = (int)(LDS_MAX / per_ref) / GROUP * GROUP;
+    return std::max(c, GROUP);
+}
+
+size_t sweep_lds(const MapFmt &f, int chunk, bool colmax) {
+    return (size_t)(chunk / TILE) * f.tile_bytes() + (colmax ? (size_t)chunk * 4 : 0);
+}
+
+// ----------------------------------------------------------------- dispatch
+template <int DT, int NP, int NKB, bool COLMAX>
+hipError_t launch_sweep_t(const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+    constexpr int rq = (DT == DT_F32) ? RQ32 : RQ;
+    auto k = sweep_kernel<DT, NP, NKB, rq, NW, COLMAX>;
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, grid, dim3(NW * 64), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int DT, bool COLMAX>
+hipError_t launch_sweep_dt(const MapFmt &f, const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+    if constexpr (DT == DT_F32) {
+        if (f.nkb == 8) return launch_sweep_t<DT_F32, 0, 8, COLMAX>(a, grid, lds, s);
+        return launch_sweep_t<DT_F32, 0, 32, COLMAX>(a, grid, lds, s);
+    } else {
+        switch (f.np) {
+        case 1: return launch_sweep_t<DT, 1, 1, COLMAX>(a, grid, lds, s);
+        case 2: return launch_sweep_t<DT, 2, 1, COLMAX>(a, grid, lds, s);
+        case 3: return launch_sweep_t<DT, 3, 1, COLMAX>(a, grid, lds, s);
+        case 4: return launch_sweep_t<DT, 4, 1, COLMAX>(a, grid, lds, s);
+        case 6: return launch_sweep_t<DT, 6, 2, COLMAX>(a, grid, lds, s);
+        case 8: return launch_sweep_t<DT, 8, 2, COLMAX>(a, grid, lds, s);
+        case 12: return launch_sweep_t<DT, 12, 3, COLMAX>(a, grid, lds, s);
+        case 16: return launch_sweep_t<DT, 16, 4, COLMAX>(a, grid, lds, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+}
+
+hipError_t launch_sweep(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s) {
+    const size_t lds = sweep_lds(f, a.chunk, colmax);
+    switch (f.dtype) {
+    case DT_F16: return colmax ? launch_sweep_dt<DT_F16, true>(f, a, grid, lds, s)
+                               : launch_sweep_dt<DT_F16, false>(f, a, grid, lds, s);
+    case DT_BF16: return colmax ? launch_sweep_dt<DT_BF16, true>(f, a, grid, lds, s)
+                                : launch_sweep_dt<DT_BF16, false>(f, a, grid, lds, s);
+    default: return colmax ? launch_sweep_dt<DT_F32, true>(f, a, grid, lds, s)
+                           : launch_sweep_dt<DT_F32, false>(f, a, grid, lds, s);
+    }
+}
+
+#define DDM_DT_SWITCH(dtype, KERNEL, ...)                                                         \
+    do {                                                                                          \
+        if ((dtype) == DT_F16) hipLaunchKernelGGL(KERNEL<DT_F16>, __VA_ARGS__);                   \
+        else if ((dtype) == DT_BF16) hipLaunchKernelGGL(KERNEL<DT_BF16>, __VA_ARGS__);            \
+        else hipLaunchKernelGGL(KERNEL<DT_F32>, __VA_ARGS__);                                     \
+    } while (0)
+
+#define DDM_CHECK(expr)                                                                           \
+    do {                                                                                          \
+        if ((expr) != hipSuccess) return DDM_ERR_HIP;                                             \
+    } while (0)
+#define DDM_CHECK_LAUNCH() DDM_CHECK(hipGetLastError())
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool map_ok(const void *p, const MapFmt &f) {
+    if (!p) return false;
+    return aligned(p, f.repack ? 2 : (size_t)(f.dtype == DT_F32 ? 4 : 16));
+}
+
+int pix_ok(int H, int W) {
+    return H >= 1 && W >= 1 && (long long)H * W <= MAX_PIX;
+}
+
+int64_t seed_count(int H, int W, int S) {
+    if (S <= 0 || H < 0 || W < 0) return -1;
+    const int h0 = S / 2;
+    const int64_t ky = H > h0 ? (H - h0 + S - 1) / S : 0;
+    const int64_t kx = W > h0 ? (W - h0 + S - 1) / S : 0;
+    return ky * kx;
+}
+
+// Repack every map of a batch into ld-strided rows when needed.
+int maybe_repack(const MapFmt &f, const void *src, long long rows, void *dst, hipStream_t s, const void **use) {
+    if (!f.repack) { *use = src; return DDM_OK; }
+    const long long total = rows * f.ld;
+    const int blocks = (int)std::min<long long>((total + 255) / 256, 65535);
+    hipLaunchKernelGGL(repack_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t *)src, f.d, (uint16_t *)dst,
+                       f.ld, rows);
+    DDM_CHECK_LAUNCH();
+    *use = dst;
+    return DDM_OK;
+}
+
+// ----------------------------------------------------------------- NN plan
+struct NnPlan {
+    MapFmt f;
+    int NQ, M, N, chunk, nchunks, qblocks;
+    size_t o_part, o_rq, o_rr, total;
+};
+
+int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p) {
+    if (NQ < 1 || M < 1 || N < 1 || N > MAX_PIX || M > MAX_PIX || NQ > MAX_PIX) return DDM_ERR_INVALID;
+    if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
+    if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
+    p->NQ = NQ; p->M = M; p->N = N;
+    const int sbr = p->f.sb_rows();
+    p->qblocks = (M + sbr - 1) / sbr;
+    int chunk = chunk_limit(p->f, false);
+    // enough workgroups to fill the chip: shrink the chunk while fewer than 2048
+    while (chunk > GROUP && (long long)p->qblocks * ((N + chunk - 1) / chunk) < 2048) chunk -= GROUP;
+    p->chunk = chunk;
+    p->nchunks = (N + chunk - 1) / chunk;
+    Bump b;
+    p->o_part = b.take((size_t)p->nchunks * M * 8);
+    p->o_rq = p->f.repack ? b.take((size_t)NQ * p->f.ld * 2) : 0;
+    p->o_rr = p->f.repack ? b.take((size_t)N * p->f.ld * 2) : 0;
+    p->total = b.off;
+    return DDM_OK;
+}
+
+// ----------------------------------------------------------------- FRM plan
+struct FrmPlan {
+    MapFmt f;
+    int B, H1, W1, N1, N2, k, kx, S, max_iter, nhalf;
+    int chunk1, chunk2, nch1, nch2, qblocks, nblk;
+    long long k_bs, cnt_bs, part_bs;
+    size_t o_u, o_v, o_conv, o_score, o_act0, o_act1, o_qr0, o_qr1, o_counts, o_part, o_mj, o_ms, o_bc, o_bo,
+        o_r1, o_r2, total;
+};
+
+int frm_chunk(const MapFmt &f, int nref, long long wg_other) {
+    int chunk = chunk_limit(f, false);
+    while (chunk > GROUP && wg_other * ((nref + chunk - 1) / chunk) < 2048) chunk -= GROUP;
+    return chunk;
+}
+
+int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int max_iter, FrmPlan *p) {
+    if (B < 1 || !pix_ok(H1, W1) || !pix_ok(H2, W2)) return DDM_ERR_INVALID;
+    if (S < 1 || max_iter < 1 || max_iter > DDM_MAX_ITER) return DDM_ERR_INVALID;
+    if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
+    if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
+    p->B = B; p->H1 = H1; p->W1 = W1; p->N1 = H1 * W1; p->N2 = H2 * W2;
+    p->S = S; p->max_iter = max_iter; p->nhalf = 2 * max_iter;
+    p->k = (int)seed_count(H1, W1, S);
+    p->kx = W1 > S / 2 ? (W1 - S / 2 + S - 1) / S : 0;
+    const int sbr = p->f.sb_rows();
+    const int kk = std::max(p->k, 1);
+    p->qblocks = (kk + sbr - 1) / sbr;
+    p->chunk2 = frm_chunk(p->f, p->N2, (long long)p->qblocks * B);
+    p->chunk1 = frm_chunk(p->f, p->N1, (long long)p->qblocks * B);
+    p->nch2 = (p->N2 + p->chunk2 - 1) / p->chunk2;
+    p->nch1 = (p->N1 + p->chunk1 - 1) / p->chunk1;
+    p->nblk = (p->N1 + CB - 1) / CB;
+    p->k_bs = kk;
+    p->cnt_bs = (long long)align_up((size_t)p->nhalf + 1, 64);
+    p->part_bs = (long long)std::max(p->nch1, p->nch2) * kk;
+    Bump b;
+    const size_t kb = (size_t)B * kk * 4;
+    p->o_u = b.take(kb); p->o_v = b.take(kb); p->o_conv = b.take(kb); p->o_score = b.take(kb);
+    p->o_act0 = b.take(kb); p->o_act1 = b.take(kb); p->o_qr0 = b.take(kb); p->o_qr1 = b.take(kb);
+    p->o_counts = b.take((size_t)B * p->cnt_bs * 4);
+    p->o_part = b.take((size_t)B * p->part_bs * 8);
+    p->o_mj = b.take((size_t)B * p->N1 * 4);
+    p->o_ms = b.take((size_t)B * p->N1 * 4);
+    p->o_bc = b.take((size_t)B * p->nblk * 4);
+    p->o_bo = b.take((size_t)B * p->nblk * 4);
+    p->o_r1 = p->f.repack ? b.take((size_t)B * p->N1 * p->f.ld * 2) : 0;
+    p->o_r2 = p->f.repack ? b.take((size_t)B * p->N2 * p->f.ld * 2) : 0;
+    p->total = b.off;
+    return DDM_OK;
+}
+
+int compact_run(const int32_t *mj, const float *ms, long long n_bs, int n, int B, int nblk, int32_t *bc, int32_t *bo,
+                int32_t *out_i, int32_t *out_j, float *out_s, long long out_bs, int32_t *out_count, hipStream_t s) {
+    hipLaunchKernelGGL(compact_count_kernel, dim3(nblk, B), dim3(256), 0, s, mj, n_bs, n, bc, nblk);
+    DDM_CHECK_LAUNCH();
+    hipLaunchKernelGGL(compact_scan_kernel, dim3(B), dim3(256), 0, s, (const int32_t *)bc, bo, nblk, out_count,
+                       (int)out_bs);
+    DDM_CHECK_LAUNCH();
+    hipLaunchKernelGGL(compact_scatter_kernel, dim3(nblk, B), dim3(256), 0, s, mj, ms, n_bs, n,
+                       (const int32_t *)bo, nblk, out_i, out_j, out_s, out_bs, (int)out_bs);
+    DDM_CHECK_LAUNCH();
+    return DDM_OK;
+}
+
+int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, int32_t *out_j, float *out_score,
+            int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *ws,
+            hipStream_t s) {
+    unsigned char *w = (unsigned char *)ws;
+    const MapFmt &f = P.f;
+    const void *m1, *m2;
+    int rc = maybe_repack(f, D1, (long long)P.B * P.N1, w + P.o_r1, s, &m1);
+    if (rc) return rc;
+    rc = maybe_repack(f, D2, (long long)P.B * P.N2, w + P.o_r2, s, &m2);
+    if (rc) return rc;
+
+    FrmState st;
+    st.u = (int32_t *)(w + P.o_u); st.v = (int32_t *)(w + P.o_v); st.conv = (int32_t *)(w + P.o_conv);
+    st.score = (float *)(w + P.o_score);
+    st.act[0] = (int32_t *)(w + P.o_act0); st.act[1] = (int32_t *)(w + P.o_act1);
+    st.qrows[0] = (int32_t *)(w + P.o_qr0); st.qrows[1] = (int32_t *)(w + P.o_qr1);
+    st.counts = (int32_t *)(w + P.o_counts);
+    st.match_j = (int32_t *)(w + P.o_mj); st.match_s = (float *)(w + P.o_ms);
+    st.k_bs = P.k_bs; st.cnt_bs = P.cnt_bs; st.n1_bs = P.N1;
+    uint64_t *part = (uint64_t *)(w + P.o_part);
+
+    const int init_blocks = (int)std::min<long long>((std::max(P.k, P.N1) + 255) / 256, 4096);
+    hipLaunchKernelGGL(frm_init_kernel, dim3(init_blocks, P.B), dim3(256), 0, s, st, P.k, std::max(P.kx, 1),
+                       P.W1, P.S, P.N1, P.nhalf);
+    DDM_CHECK_LAUNCH();
+
+    const long long b1 = (long long)P.N1 * f.ld * f.esz, b2 = (long long)P.N2 * f.ld * f.esz;
+    const int upd_blocks = (std::max(P.k, 1) * 16 + 255) / 256;
+    if (P.k > 0) {
+        for (int t = 0; t < P.max_iter; ++t) {
+            for (int dir = 0; dir < 2; ++dir) {
+                const int h = 2 * t + dir;
+                SweepArgs a{};
+                a.Q = (const unsigned char *)(dir == 0 ? m1 : m2);
+                a.R = (const unsigned char *)(dir == 0 ? m2 : m1);
+                a.q_bs = dir == 0 ? b1 : b2;
+                a.r_bs = dir == 0 ? b2 : b1;
+                a.qrows = st.qrows[h & 1]; a.qrows_bs = P.k_bs;
+                a.qcount = st.counts + h; a.qcount_bs = P.cnt_bs;
+                a.rowpart = part; a.rowpart_bs = P.part_bs;
+                a.colpart = nullptr; a.colpart_bs = 0;
+                a.nq = P.k;
+                a.nref = dir == 0 ? P.N2 : P.N1;
+                a.ld = f.ld;
+                a.chunk = dir == 0 ? P.chunk2 : P.chunk1;
+                a.nchunks = dir == 0 ? P.nch2 : P.nch1;
+                a.sb_per_wg = 1;
+                a.rowcap = (int)P.k_bs;
+                DDM_CHECK(launch_sweep(f, false, a, dim3(a.nchunks, P.qblocks, P.B), s));
+
+                ResolveArgs r{};
+                r.rowpart = part; r.rowpart_bs = P.part_bs; r.nchunks = a.nchunks; r.rowcap = (int)P.k_bs;
+                r.Q = a.Q; r.q_bs = a.q_bs; r.qrows = nullptr; r.qrows_bs = 0;
+                r.qcount = nullptr; r.qcount_bs = 0; r.nq = P.k;
+                r.R = a.R; r.r_bs = a.r_bs; r.nref = a.nref; r.ld = f.ld; r.d = f.d;
+                DDM_DT_SWITCH(f.dtype, frm_update_kernel, dim3(upd_blocks, P.B), dim3(256), 0, s, r, st, h, dir,
+                              t + 1);
+                DDM_CHECK_LAUNCH();
+            }
+        }
+    }
+    const int col_blocks = (int)std::min<long long>((std::max(P.k, 1) + 255) / 256, 4096);
+    hipLaunchKernelGGL(frm_collect_kernel, dim3(col_blocks, P.B), dim3(256), 0, s, st, P.k, seed_state,
+                       (const int32_t *)st.counts, query_counts, P.nhalf);
+    DDM_CHECK_LAUNCH();
+    return compact_run(st.match_j, st.match_s, P.N1, P.N1, P.B, P.nblk, (int32_t *)(w + P.o_bc),
+                       (int32_t *)(w + P.o_bo), out_i, out_j, out_score, capacity, out_count, s);
+}
+
+// -------------------------------------------------------------- mutual plan
+struct MutualPlan {
+    MapFmt f;
+    int N1, N2, chunk, nchunks, sb_per_wg, qblocks, nblk;
+    size_t o_part, o_col, o_cmax, o_mj, o_ms, o_bc, o_bo, o_r1, o_r2, total;
+};
+
+int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p) {
+    if (!pix_ok(H1, W1) || !pix_ok(H2, W2)) return DDM_ERR_INVALID;
+    if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
+    if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
+    p->N1 = H1 * W1; p->N2 = H2 * W2;
+    const int sbr = p->f.sb_rows();
+    const int nsb = (p->N1 + sbr - 1) / sbr;
+    int chunk = chunk_limit(p->f, true);
+    // at least ~2 workgroups per CU along the chunk axis alone when the map is small
+    while (chunk > GROUP && (long long)nsb * ((p->N2 + chunk - 1) / chunk) < 512) chunk -= GROUP;
+    p->chunk = chunk;
+    p->nchunks = (p->N2 + chunk - 1) / chunk;
+    // query sub-blocks per workgroup: aim at ~2048 workgroups, fewer column partials
+    const long long want_qblocks = std::max<long long>(1, 2048 / p->nchunks);
+    p->sb_per_wg = (int)std::max<long long>(1, (nsb + want_qblocks - 1) / want_qblocks);
+    p->qblocks = (nsb + p->sb_per_wg - 1) / p->sb_per_wg;
+    p->nblk = (p->N1 + CB - 1) / CB;
+    Bump b;
+    p->o_part = b.take((size_t)p->nchunks * p->N1 * 8);
+    p->o_col = b.take((size_t)p->qblocks * p->N2 * 4);
+    p->o_cmax = b.take((size_t)p->N2 * 4);
+    p->o_mj = b.take((size_t)p->N1 * 4);
+    p->o_ms = b.take((size_t)p->N1 * 4);
+    p->o_bc = b.take((size_t)p->nblk * 4);
+    p->o_bo = b.take((size_t)p->nblk * 4);
+    p->o_r1 = p->f.repack ? b.take((size_t)p->N1 * p->f.ld * 2) : 0;
+    p->o_r2 = p->f.repack ? b.take((size_t)p->N2 * p->f.ld * 2) : 0;
+    p->total = b.off;
+    return DDM_OK;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+// ===================================================================== C ABI
+extern "C" {
+
+const char *ddm_status_str(int status) {
+    switch (status) {
+    case DDM_OK: return "ok";
+    case DDM_ERR_INVALID: return "invalid argument";
+    case DDM_ERR_CAPACITY: return "output capacity too small";
+    case DDM_ERR_WORKSPACE: return "workspace missing or too small";
+    case DDM_ERR_UNSUPPORTED: return "unsupported dtype or descriptor dimension";
+    case DDM_ERR_HIP: return "HIP error while enqueueing";
+    default: return "unknown status";
+    }
+}
+
+int64_t ddm_seed_count(int H, int W, int grid_stride) { return seed_count(H, W, grid_stride); }
+
+}  // extern "C"
+
+extern "C" {
+
+size_t ddm_nn_workspace_bytes(int NQ, int M, int N, int d, int dtype) {
+    NnPlan P;
+    return nn_plan(NQ, M, N, d, dtype, &P) == DDM_OK ? P.total : 0;
+}
+
+int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, int N, int d, int dtype,
+           int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    NnPlan P;
+    int rc = nn_plan(NQ, M, N, d, dtype, &P);
+    if (rc) return rc;
+    if (!map_ok(Q, P.f) || !map_ok(R, P.f) || !out_idx || !out_score) return DDM_ERR_INVALID;
+    if (!q_rows && NQ < M) return DDM_ERR_INVALID;
+    if (!workspace || workspace_bytes < P.total) return DDM_ERR_WORKSPACE;
+    unsigned char *w = (unsigned char *)workspace;
+    const void *q, *r;
+    rc = maybe_repack(P.f, Q, NQ, w + P.o_rq, stream, &q);
+    if (rc) return rc;
+    rc = maybe_repack(P.f, R, N, w + P.o_rr, stream, &r);
+    if (rc) return rc;
+    SweepArgs a{};
+    a.Q = (const unsigned char *)q; a.R = (const unsigned char *)r; a.qrows = q_rows;
+    a.rowpart = (uint64_t *)(w + P.o_part);
+    a.nq = M; a.nref = N; a.ld = P.f.ld; a.chunk = P.chunk; a.nchunks = P.nchunks; a.sb_per_wg = 1;
+    a.rowcap = M;
+    DDM_CHECK(launch_sweep(P.f, false, a, dim3(P.nchunks, P.qblocks, 1), stream));
+    ResolveArgs ra{};
+    ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = M;
+    ra.Q = a.Q; ra.qrows = q_rows; ra.nq = M; ra.R = a.R; ra.nref = N; ra.ld = P.f.ld; ra.d = d;
+    const int blocks = (M * 16 + 255) / 256;
+    DDM_DT_SWITCH(P.f.dtype, nn_resolve_kernel, dim3(blocks), dim3(256), 0, stream, ra, out_idx, out_score);
+    DDM_CHECK_LAUNCH();
+    return DDM_OK;
+}
+
+size_t ddm_frm_workspace_bytes(int B, int H1, int W1, int H2, int W2, int d, int dtype, int grid_stride,
+                               int max_iter) {
+    FrmPlan P;
+    return frm_plan(B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P) == DDM_OK ? P.total : 0;
+}
+
+static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                     int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score,
+                     int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    FrmPlan P;
+    int rc = frm_plan(B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P);
+    if (rc) return rc;
+    if (!map_ok(D1, P.f) || !map_ok(D2, P.f)) return DDM_ERR_INVALID;
+    if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
+    if (capacity < P.k) return DDM_ERR_CAPACITY;
+    if (!workspace || workspace_bytes < P.total) return DDM_ERR_WORKSPACE;
+    return frm_run(P, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts, workspace,
+                   stream);
+}
+
+int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                  int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
+                  int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, out_i, out_j, out_score, capacity,
+                     out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
+}
+
+int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                          int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score,
+                          int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return frm_entry(B, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, out_i, out_j, out_score, capacity,
+                     out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
+}
+
+size_t ddm_mutual_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype) {
+    MutualPlan P;
+    return mutual_plan(H1, W1, H2, W2, d, dtype, &P) == DDM_OK ? P.total : 0;
+}
+
+int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype, int32_t *out_i,
+                  int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count, int32_t *nn12, float *s12,
+                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    MutualPlan P;
+    int rc = mutual_plan(H1, W1, H2, W2, d, dtype, &P);
+    if (rc) return rc;
+    if (!map_ok(D1, P.f) || !map_ok(D2, P.f)) return DDM_ERR_INVALID;
+    if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
+    if ((nn12 == nullptr) != (s12 == nullptr)) return DDM_ERR_INVALID;
+    if (capacity < std::min(P.N1, P.N2)) return DDM_ERR_CAPACITY;
+    if (!workspace || workspace_bytes < P.total) return DDM_ERR_WORKSPACE;
+    unsigned char *w = (unsigned char *)workspace;
+    const void *m1, *m2;
+    rc = maybe_repack(P.f, D1, P.N1, w + P.o_r1, stream, &m1);
+    if (rc) return rc;
+    rc = maybe_repack(P.f, D2, P.N2, w + P.o_r2, stream, &m2);
+    if (rc) return rc;
+    SweepArgs a{};
+    a.Q = (const unsigned char *)m1; a.R = (const unsigned char *)m2;
+    a.rowpart = (uint64_t *)(w + P.o_part);
+    a.colpart = (uint32_t *)(w + P.o_col);
+    a.nq = P.N1; a.nref = P.N2; a.ld = P.f.ld; a.chunk = P.chunk; a.nchunks = P.nchunks;
+    a.sb_per_wg = P.sb_per_wg; a.rowcap = P.N1;
+    DDM_CHECK(launch_sweep(P.f, true, a, dim3(P.nchunks, P.qblocks, 1), stream));
+    uint32_t *cmax = (uint32_t *)(w + P.o_cmax);
+    hipLaunchKernelGGL(colmax_merge_kernel, dim3((P.N2 + 255) / 256), dim3(256), 0, stream,
+                       (const uint32_t *)a.colpart, P.qblocks, P.N2, cmax);
+    DDM_CHECK_LAUNCH();
+    ResolveArgs ra{};
+    ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = P.N1;
+    ra.Q = a.Q; ra.nq = P.N1; ra.R = a.R; ra.nref = P.N2; ra.ld = P.f.ld; ra.d = d;
+    int32_t *mj = (int32_t *)(w + P.o_mj);
+    float *ms = (float *)(w + P.o_ms);
+    DDM_DT_SWITCH(P.f.dtype, mutual_rows_kernel, dim3((P.N1 * 16 + 255) / 256), dim3(256), 0, stream, ra,
+                  (const uint32_t *)cmax, mj, ms, nn12, s12);
+    DDM_CHECK_LAUNCH();
+    return compact_run(mj, ms, P.N1, P.N1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo), out_i, out_j,
+                       out_score, capacity, out_count, stream);
+}
+
+}  // extern "C"

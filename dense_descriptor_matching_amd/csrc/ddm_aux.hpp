@@ -1,0 +1,311 @@
+// ddm_aux.hpp -- the kernels around the sweep: index resolution, the FRM state
+// machine (seed grid, cycle tests, active-set compaction), the mutual check and
+// the ordered output compaction.
+//
+// FRM follows the fast_reciprocal_NNs routine quoted in "DUSt3R和MASt3R论文阅读"
+// (Staskaer blog, section MASt3R matching): seeds on the stride-S grid, one
+// forward and one backward NN query per iteration for the seeds still active,
+// a seed stops once its new image-2 pixel equals the previous one (forward
+// test) or its new image-1 pixel equals the previous one (backward test), at
+// most max_iter iterations, and the stopped seeds give unique pairs sorted by
+// the image-1 index. The reciprocal set follows the FRM paragraph of the
+// "MASt3R" note on cv-learn.com (section 手法とアーキテクチャ).
+#pragma once
+#include "ddm_sweep.hpp"
+
+namespace ddm {
+
+// ---------------------------------------------------------------------------
+// Index resolution. A query's row partials (one per reference chunk) hold the
+// maximum score and the (group, slot) that produced it; the exact reference
+// is one of the 16 consecutive references group*256 + slot*16 + t. Sixteen
+// lanes recompute those dots (fp32 FMA on the stored values) and keep the
+// largest, lowest t on ties. The reported score is the matrix-core maximum.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float dot_rows(const unsigned char *a, const unsigned char *b, int d) {
+    float s = 0.f;
+    for (int k = 0; k < d; ++k) s = fmaf(Tr<DT>::elem(a, k), Tr<DT>::elem(b, k), s);
+    return s;
+}
+
+// Called by all 16 lanes of a DPP row (sub = lane & 15) for one query x.
+template <int DT>
+__device__ __forceinline__ void resolve_one(const uint64_t *part, int nchunks, long long rowcap, int x,
+                                            const unsigned char *qp, const unsigned char *R, int nref, int ld,
+                                            int d, int sub, int *j_out, float *s_out) {
+    constexpr int ESZ = Tr<DT>::ESZ;
+    uint64_t k = 0;
+    for (int ch = sub; ch < nchunks; ch += 16) {
+        const uint64_t v = part[(long long)ch * rowcap + x];
+        k = v > k ? v : k;
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        const uint64_t o = __shfl_xor(k, m, 16);
+        k = o > k ? o : k;
+    }
+    const float mval = fkey_inv((uint32_t)(k >> 32));
+    const uint32_t id = ~(uint32_t)k;
+    const int j = (int)((id >> 4) * GROUP + (id & 15u) * TILE) + sub;
+    float s = -INFINITY;
+    if (j < nref) s = dot_rows<DT>(qp, R + (long long)j * ld * ESZ, d);
+    int bj = j < nref ? j : 0x7fffffff;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        const float os = __shfl_xor(s, m, 16);
+        const int oj = __shfl_xor(bj, m, 16);
+        if (os > s || (os == s && oj < bj)) { s = os; bj = oj; }
+    }
+    // every valid query has a partial from every chunk, so bj < nref; clamp anyway so
+    // that a bad index can never become an out-of-range gather downstream
+    *j_out = bj < nref ? bj : nref - 1;
+    *s_out = mval;
+}
+
+struct ResolveArgs {
+    const uint64_t *rowpart; long long rowpart_bs; int nchunks; int rowcap;
+    const unsigned char *Q; long long q_bs; const int32_t *qrows; long long qrows_bs;
+    const int32_t *qcount; long long qcount_bs; int nq;
+    const unsigned char *R; long long r_bs; int nref; int ld; int d;
+};
+
+// Plain NN output: out_idx[x], out_score[x] for every query.
+template <int DT>
+__global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, int32_t *out_idx, float *out_score) {
+    const int x = (blockIdx.x * 256 + threadIdx.x) >> 4, sub = threadIdx.x & 15;
+    if (x >= a.nq) return;
+    const int qrow = a.qrows ? a.qrows[x] : x;
+    int j; float s;
+    resolve_one<DT>(a.rowpart, a.nchunks, a.rowcap, x, a.Q + (long long)qrow * a.ld * Tr<DT>::ESZ, a.R, a.nref,
+                    a.ld, a.d, sub, &j, &s);
+    if (sub == 0) { out_idx[x] = j; out_score[x] = s; }
+}
+
+// ---------------------------------------------------------------------------
+// Mutual NN: column maxima over query blocks, then per row (i, j = NN_2(i)) is
+// reciprocal iff column j's maximum equals row i's maximum (both are the same
+// matrix-core value, compared as order-preserving keys).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) colmax_merge_kernel(const uint32_t *colpart, int nqblk, int nref,
+                                                           uint32_t *colmax) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= nref) return;
+    uint32_t m = 0;
+    for (int b = 0; b < nqblk; ++b) m = max(m, colpart[(long long)b * nref + j]);
+    colmax[j] = m;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint32_t *colmax, int32_t *match_j,
+                                                          float *match_s, int32_t *nn12, float *s12) {
+    const int x = (blockIdx.x * 256 + threadIdx.x) >> 4, sub = threadIdx.x & 15;
+    if (x >= a.nq) return;
+    int j; float s;
+    resolve_one<DT>(a.rowpart, a.nchunks, a.rowcap, x, a.Q + (long long)x * a.ld * Tr<DT>::ESZ, a.R, a.nref,
+                    a.ld, a.d, sub, &j, &s);
+    if (sub == 0) {
+        const bool mutual = colmax[j] == fkey(s);
+        match_j[x] = mutual ? j : -1;
+        match_s[x] = s;
+        if (nn12) { nn12[x] = j; s12[x] = s; }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FRM state. Per pair: u[k], v[k], score[k], conv[k], two active lists (seed
+// ids) with their query rows, and the per-half-step active counts
+// counts[0 .. 2*max_iter] (counts[h] = queries of half-step h).
+// ---------------------------------------------------------------------------
+struct FrmState {
+    int32_t *u, *v, *conv;
+    float *score;
+    int32_t *act[2], *qrows[2];
+    int32_t *counts;
+    int32_t *match_j; float *match_s;
+    long long k_bs;        // elements between pairs for the k-sized arrays
+    long long cnt_bs;      // elements between pairs for counts
+    long long n1_bs;       // elements between pairs for match arrays
+};
+
+// Seed grid (rows S/2 + S*n < H1, columns S/2 + S*n < W1, p = x + W1*y,
+// ascending) and the initial state; also clears the dense match array.
+__global__ void __launch_bounds__(256) frm_init_kernel(FrmState st, int k, int kx, int W1, int S, int N1,
+                                                       int nhalf) {
+    const int pair = blockIdx.y;
+    const long long ko = pair * st.k_bs;
+    for (int a = blockIdx.x * 256 + threadIdx.x; a < k; a += gridDim.x * 256) {
+        const int y = S / 2 + (a / kx) * S, x = S / 2 + (a % kx) * S;
+        const int p = x + W1 * y;
+        st.u[ko + a] = p; st.v[ko + a] = -1; st.conv[ko + a] = -1; st.score[ko + a] = 0.f;
+        st.act[0][ko + a] = a; st.qrows[0][ko + a] = p;
+    }
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < N1; i += gridDim.x * 256) st.match_j[pair * st.n1_bs + i] = -1;
+    if (blockIdx.x == 0)
+        for (int h = threadIdx.x; h <= nhalf; h += 256) st.counts[pair * st.cnt_bs + h] = (h == 0) ? k : 0;
+}
+
+// One half-step's update: resolve each active query, apply the cycle test and
+// append the seeds that stay active to the next list (wave ballot + one atomic
+// per wave; list order does not affect any result).
+template <int DT>
+__global__ void __launch_bounds__(256) frm_update_kernel(ResolveArgs a, FrmState st, int h, int backward,
+                                                         int iter) {
+    const int pair = blockIdx.y;
+    const int cur = h & 1, nxt = cur ^ 1;
+    const long long ko = pair * st.k_bs;
+    const int32_t *counts = st.counts + pair * st.cnt_bs;
+    const int nq = counts[h];
+    const int x = (blockIdx.x * 256 + threadIdx.x) >> 4, sub = threadIdx.x & 15;
+    const int lane = threadIdx.x & 63;
+    bool keep = false;
+    int seed = 0, j = 0;
+    if (x < nq) {
+        seed = st.act[cur][ko + x];
+        const int qrow = st.qrows[cur][ko + x];
+        float s;
+        resolve_one<DT>(a.rowpart + pair * a.rowpart_bs, a.nchunks, a.rowcap, x,
+                        a.Q + pair * a.q_bs + (long long)qrow * a.ld * Tr<DT>::ESZ, a.R + pair * a.r_bs, a.nref,
+                        a.ld, a.d, sub, &j, &s);
+        if (sub == 0) {
+            if (!backward) {
+                keep = (j != st.v[ko + seed]);
+                st.v[ko + seed] = j;
+                st.score[ko + seed] = s;
+            } else {
+                keep = (j != st.u[ko + seed]);
+                st.u[ko + seed] = j;
+            }
+            if (!keep) st.conv[ko + seed] = iter;
+        }
+    }
+    // stream compaction of the seeds that stay active
+    const uint64_t ball = __ballot(keep);
+    const int n = __popcll(ball);
+    int base = 0;
+    if (n > 0) {
+        if (lane == 0) base = atomicAdd(st.counts + pair * st.cnt_bs + h + 1, n);
+        base = __shfl(base, 0);
+        if (keep) {
+            const int pos = base + __popcll(ball & ((1ull << lane) - 1ull));
+            st.act[nxt][ko + pos] = seed;
+            st.qrows[nxt][ko + pos] = j;
+        }
+    }
+}
+
+// Converged seeds -> dense match array indexed by image-1 pixel (every seed
+// that reaches pixel u reports the same v and score), optional seed states.
+__global__ void __launch_bounds__(256) frm_collect_kernel(FrmState st, int k, int32_t *seed_state,
+                                                          const int32_t *counts_in, int32_t *query_counts,
+                                                          int nhalf) {
+    const int pair = blockIdx.y;
+    const long long ko = pair * st.k_bs;
+    for (int a = blockIdx.x * 256 + threadIdx.x; a < k; a += gridDim.x * 256) {
+        const int u = st.u[ko + a], v = st.v[ko + a], it = st.conv[ko + a];
+        if (it >= 0) {
+            st.match_j[pair * st.n1_bs + u] = v;
+            st.match_s[pair * st.n1_bs + u] = st.score[ko + a];
+        }
+        if (seed_state) {
+            int32_t *ss = seed_state + (pair * (long long)k + a) * 4;
+            ss[0] = u; ss[1] = v; ss[2] = it; ss[3] = 0;
+        }
+    }
+    if (query_counts && blockIdx.x == 0)
+        for (int h = threadIdx.x; h < nhalf; h += 256)
+            query_counts[pair * (long long)nhalf + h] = counts_in[pair * st.cnt_bs + h];
+}
+
+// ---------------------------------------------------------------------------
+// Ordered compaction of a dense match array (j >= 0 marks a pair) into sorted
+// (i, j, score) lists: per-block counts, one scan per pair, scatter.
+// ---------------------------------------------------------------------------
+constexpr int CB = 1024;   // entries per compaction block (256 threads x 4)
+
+__global__ void __launch_bounds__(256) compact_count_kernel(const int32_t *match_j, long long n_bs, int n,
+                                                            int32_t *blockcnt, int nblk) {
+    const int pair = blockIdx.y;
+    const int32_t *mj = match_j + pair * n_bs;
+    int c = 0;
+    const int base = blockIdx.x * CB;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int i = base + t * 256 + threadIdx.x;
+        c += (i < n && mj[i] >= 0) ? 1 : 0;
+    }
+    __shared__ int red[4];
+    for (int m = 32; m > 0; m >>= 1) c += __shfl_xor(c, m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) blockcnt[pair * nblk + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ void __launch_bounds__(256) compact_scan_kernel(const int32_t *blockcnt, int32_t *blockoff, int nblk,
+                                                           int32_t *out_count, int capacity) {
+    const int pair = blockIdx.x;
+    __shared__ int carry;
+    __shared__ int wsum[4];
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int b0 = 0; b0 < nblk; b0 += 256) {
+        const int b = b0 + threadIdx.x;
+        const int v = b < nblk ? blockcnt[pair * nblk + b] : 0;
+        int incl = v;
+        for (int m = 1; m < 64; m <<= 1) {
+            const int o = __shfl_up(incl, m);
+            if (lane >= m) incl += o;
+        }
+        if (lane == 63) wsum[w] = incl;
+        __syncthreads();
+        int woff = 0;
+        for (int q = 0; q < w; ++q) woff += wsum[q];
+        if (b < nblk) blockoff[pair * nblk + b] = carry + woff + incl - v;
+        __syncthreads();
+        if (threadIdx.x == 0) carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out_count[pair] = carry < capacity ? carry : capacity;
+}
+
+__global__ void __launch_bounds__(256) compact_scatter_kernel(const int32_t *match_j, const float *match_s,
+                                                              long long n_bs, int n, const int32_t *blockoff,
+                                                              int nblk, int32_t *out_i, int32_t *out_j,
+                                                              float *out_s, long long out_bs, int capacity) {
+    const int pair = blockIdx.y;
+    const int32_t *mj = match_j + pair * n_bs;
+    const float *ms = match_s + pair * n_bs;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __shared__ int wcnt[4];
+    int off = blockoff[pair * nblk + blockIdx.x];
+    for (int t = 0; t < 4; ++t) {
+        const int i = blockIdx.x * CB + t * 256 + threadIdx.x;
+        const bool valid = i < n && mj[i] >= 0;
+        const uint64_t ball = __ballot(valid);
+        if (lane == 0) wcnt[w] = __popcll(ball);
+        __syncthreads();
+        int woff = 0;
+        for (int q = 0; q < w; ++q) woff += wcnt[q];
+        const int rank = off + woff + __popcll(ball & ((1ull << lane) - 1ull));
+        if (valid && rank < capacity) {
+            const long long pos = pair * out_bs + rank;
+            out_i[pos] = i; out_j[pos] = mj[i]; out_s[pos] = ms[i];
+        }
+        off += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+        __syncthreads();
+    }
+}
+
+// Zero-padded copy [n][d] -> [n][ld] for maps whose rows are not a whole
+// number of 16-byte pieces of a supported width.
+__global__ void __launch_bounds__(256) repack_kernel(const uint16_t *src, int d, uint16_t *dst, int ld, long long n) {
+    const long long total = n * ld;
+    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        const long long r = e / ld;
+        const int k = (int)(e - r * ld);
+        dst[e] = k < d ? src[r * d + k] : (uint16_t)0;
+    }
+}
+
+}  // namespace ddm

@@ -1,0 +1,341 @@
+// ddm_sweep.hpp -- fused dot-product + running arg-max sweep on CDNA4 matrix cores.
+//
+// One launch scores a set of query rows against every row of a reference map
+// without ever materialising the score matrix. Nearest neighbour = arg-max of
+// the dot product ("MASt3R" note on cv-learn.com, section
+// 手法とアーキテクチャ, FRM paragraph); the exhaustive reciprocal set of the
+// same paragraph additionally needs every column's maximum, which the COLMAX
+// variant produces in the same pass.
+//
+// Work decomposition
+//   grid.x  = reference chunk (CHUNK rows, a multiple of 256), staged once in LDS
+//   grid.y  = query block (sb_per_wg sub-blocks of NW*RQ*16 rows)
+//   grid.z  = independent pair (batched calls)
+//   Each wave keeps RQ query tiles of 16 rows resident in VGPRs as MFMA A
+//   operands and streams the chunk's 16-row reference tiles from LDS as B
+//   operands with v_mfma_f32_16x16x32_{f16,bf16} (v_mfma_f32_16x16x4_f32 for
+//   fp32 maps), K padded to 32 with zeros in A only.
+//
+// Epilogue (the part that bounds this kernel at d = 24)
+//   MFMA output lane l holds reference slot c = l % 16 and query rows
+//   4*(l/16) + r, r = 0..3. Row direction: per register a running maximum over
+//   a group of G = 16 tiles with one v_max3_f32 per two scores, then one
+//   compare + select per register and group to remember which group held the
+//   maximum (lazy index). Inside a group the 256 references are laid out so
+//   that slot c of tile t is reference 16*c + t: the 16 candidates of one
+//   (group, slot) are contiguous, and (group, slot, t) order equals reference
+//   order, so the lowest-index tie-break survives. The exact index inside the
+//   group is recovered later by recomputing 16 candidate dots (ddm_resolve).
+//   Column direction (COLMAX): in-lane v_max3 chain over the wave's rows, two
+//   lane swaps (v_permlane32_swap, v_permlane16_swap) pack four tiles' column
+//   maxima into one register, one ds_max_u32 of order-preserving keys per four
+//   tiles into an LDS column array, flushed once per workgroup.
+//
+// Invalid reference slots (chunk tail) hold NaN, whose scores are NaN and are
+// ignored by v_max3 (maxNum semantics); invalid query rows duplicate the last
+// valid row, which changes no column maximum and is never written back.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ddm {
+
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+constexpr int TILE = 16;            // references per MFMA tile
+constexpr int G = 16;               // tiles per index group
+constexpr int GROUP = TILE * G;     // references per index group
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 == +0.
+__device__ __forceinline__ uint32_t fkey(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+template <int DT> struct Tr;
+template <> struct Tr<DT_F16> {
+    static constexpr int E = 8, PS = 16, ESZ = 2;     // elements / bytes per lane piece
+    using raw = u32x4_t;
+    __device__ static f32x4_t mma(raw a, raw b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+    }
+    __device__ static raw nan_piece() { return raw{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u}; }
+    __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
+    __device__ static float elem(const unsigned char *p, int k) {
+        return (float)reinterpret_cast<const _Float16 *>(p)[k];
+    }
+};
+template <> struct Tr<DT_BF16> {
+    static constexpr int E = 8, PS = 16, ESZ = 2;
+    using raw = u32x4_t;
+    __device__ static f32x4_t mma(raw a, raw b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+    __device__ static raw nan_piece() { return raw{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}; }
+    __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
+    __device__ static float elem(const unsigned char *p, int k) {
+        uint32_t u = (uint32_t)reinterpret_cast<const uint16_t *>(p)[k] << 16;
+        return __uint_as_float(u);
+    }
+};
+template <> struct Tr<DT_F32> {
+    static constexpr int E = 1, PS = 4, ESZ = 4;
+    using raw = uint32_t;
+    __device__ static f32x4_t mma(raw a, raw b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a), __uint_as_float(b), c, 0, 0, 0);
+    }
+    __device__ static raw nan_piece() { return 0x7fc00000u; }
+    __device__ static raw zero() { return 0u; }
+    __device__ static float elem(const unsigned char *p, int k) {
+        return reinterpret_cast<const float *>(p)[k];
+    }
+};
+
+struct SweepArgs {
+    const unsigned char *Q;      // query map of pair 0
+    const unsigned char *R;      // reference map of pair 0
+    const int32_t *qrows;        // optional gather list (row of Q for each query)
+    const int32_t *qcount;       // optional device query count (else nq)
+    uint64_t *rowpart;           // [pair][nchunks][rowcap] row partial keys
+    uint32_t *colpart;           // [pair][nqblk][nref] column partial keys (COLMAX)
+    long long q_bs, r_bs;        // bytes between pairs
+    long long qrows_bs, qcount_bs, rowpart_bs, colpart_bs;   // elements between pairs
+    int nq;                      // query count (upper bound when qcount is set)
+    int nref;                    // reference rows per pair
+    int ld;                      // row stride in elements
+    int chunk;                   // references per chunk (multiple of GROUP)
+    int nchunks;
+    int sb_per_wg;               // query sub-blocks per workgroup
+    int rowcap;                  // rows per chunk slice of rowpart
+};
+
+// Row-partial key: high word = order-preserving key of the row maximum, low
+// word = ~(global group << 4 | slot): the u64 maximum prefers the larger score,
+// then the lower (group, slot), i.e. the lower reference index.
+__device__ __forceinline__ uint64_t row_key(float m, uint32_t gslot) {
+    return ((uint64_t)fkey(m) << 32) | (uint64_t)(~gslot);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+// All-reduce over the 16 lanes of a DPP row: xor 1, xor 2 (quad permutes),
+// half-row mirror, row mirror.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t row16_min(uint32_t x) {
+    x = min(x, dpp_u<0xB1>(x));
+    x = min(x, dpp_u<0x4E>(x));
+    x = min(x, dpp_u<0x141>(x));
+    x = min(x, dpp_u<0x140>(x));
+    return x;
+}
+
+// NP = pieces (of E elements) per stored row; 0 = runtime (fp32 path).
+// NKB = 32-wide (fp16/bf16) or 4-wide (fp32) K blocks.
+template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
+__global__ void __launch_bounds__(NW * 64)
+sweep_kernel(SweepArgs p)
+{
+    using T = Tr<DT>;
+    using raw = typename T::raw;
+    constexpr int E = T::E, PS = T::PS, ESZ = T::ESZ;
+    constexpr int SB_ROWS = NW * RQ * 16;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int pair = blockIdx.z, chunk_id = blockIdx.x, qblk = blockIdx.y;
+    const int nq = p.qcount ? p.qcount[pair * p.qcount_bs] : p.nq;
+    const int n_sb = (nq + SB_ROWS - 1) / SB_ROWS;
+    const int sb_first = qblk * p.sb_per_wg;
+    if (sb_first >= n_sb) return;
+    const int sb_last = min(sb_first + p.sb_per_wg, n_sb);
+
+    const unsigned char *Q = p.Q + pair * p.q_bs;
+    const unsigned char *R = p.R + pair * p.r_bs;
+    const int32_t *qrows = p.qrows ? p.qrows + pair * p.qrows_bs : nullptr;
+
+    const int np = NP > 0 ? NP : p.ld / E;          // pieces per row
+    const int TB = np * 16 * PS;                    // LDS bytes per tile
+    const int nkb = NP > 0 ? NKB : (np + 3) / 4;    // K blocks in use
+    const int r0 = chunk_id * p.chunk;
+    const int nvalid = min(p.chunk, p.nref - r0);
+    const int ngroups = (nvalid + GROUP - 1) / GROUP;
+    const int nslots = ngroups * GROUP;
+
+    // ---- stage the chunk in LDS: slot c of tile t of group q <- reference q*256 + 16*c + t
+    for (int qq = tid; qq < nslots * np; qq += NW * 64) {
+        const int r = qq / np, pc = qq - r * np;
+        raw v;
+        if (r < nvalid)
+            v = *reinterpret_cast<const raw *>(R + ((long long)(r0 + r) * p.ld + pc * E) * ESZ);
+        else
+            v = T::nan_piece();
+        const int grp = r / GROUP, w = r % GROUP;
+        const int tile = grp * G + (w % TILE);
+        const int c = w / TILE;
+        *reinterpret_cast<raw *>(lds + tile * TB + pc * 16 * PS + c * PS) = v;
+    }
+    uint32_t *colmax_lds = reinterpret_cast<uint32_t *>(lds + (size_t)(p.chunk / TILE) * TB);
+    if constexpr (COLMAX) {
+        for (int s = tid; s < nslots; s += NW * 64) colmax_lds[s] = 0u;
+    }
+    __syncthreads();
+
+    const int c = lane & 15, g = lane >> 4;
+    int boff[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        const int pc = min(kb * 4 + g, np - 1);     // lanes past the last piece re-read it; A is 0 there
+        boff[kb] = pc * 16 * PS + c * PS;
+    }
+    const uint32_t gbase = (uint32_t)chunk_id * (uint32_t)(p.chunk / GROUP);
+
+    for (int sb = sb_first; sb < sb_last; ++sb) {
+        const int row0 = sb * SB_ROWS + wave * RQ * 16;
+        if (row0 >= nq) break;
+
+        raw a[RQ][NKB];
+#pragma unroll
+        for (int qt = 0; qt < RQ; ++qt) {
+            int rr = min(row0 + qt * 16 + c, nq - 1);
+            const int qrow = qrows ? qrows[rr] : rr;
+            const unsigned char *qp = Q + (long long)qrow * p.ld * ESZ;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int pc = kb * 4 + g;
+                a[qt][kb] = (pc < np) ? *reinterpret_cast<const raw *>(qp + pc * PS) : T::zero();
+            }
+        }
+
+        float best[RQ][4];
+        int gid[RQ][4];
+#pragma unroll
+        for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { best[qt][r] = -INFINITY; gid[qt][r] = 0; }
+
+        for (int grp = 0; grp < ngroups; ++grp) {
+            const unsigned char *gb = lds + grp * G * TB;
+            float nb[RQ][4];
+#pragma unroll
+            for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) nb[qt][r] = best[qt][r];
+            float colm[4];
+#pragma unroll
+            for (int tp = 0; tp < G; tp += 2) {
+                raw b0[NKB], b1[NKB];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    b0[kb] = *reinterpret_cast<const raw *>(gb + tp * TB + boff[kb]);
+                    b1[kb] = *reinterpret_cast<const raw *>(gb + (tp + 1) * TB + boff[kb]);
+                }
+                f32x4_t acc0[RQ], acc1[RQ];
+#pragma unroll
+                for (int qt = 0; qt < RQ; ++qt) {
+                    acc0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    acc1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        if (NP > 0 || kb < nkb) {
+                            acc0[qt] = T::mma(a[qt][kb], b0[kb], acc0[qt]);
+                            acc1[qt] = T::mma(a[qt][kb], b1[kb], acc1[qt]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        nb[qt][r] = fmaxf(fmaxf(nb[qt][r], acc0[qt][r]), acc1[qt][r]);
+                if constexpr (COLMAX) {
+                    float m0 = fmaxf(acc0[0][0], acc0[0][1]);
+                    float m1 = fmaxf(acc1[0][0], acc1[0][1]);
+                    m0 = fmaxf(fmaxf(m0, acc0[0][2]), acc0[0][3]);
+                    m1 = fmaxf(fmaxf(m1, acc1[0][2]), acc1[0][3]);
+#pragma unroll
+                    for (int qt = 1; qt < RQ; ++qt) {
+                        m0 = fmaxf(fmaxf(m0, acc0[qt][0]), acc0[qt][1]);
+                        m0 = fmaxf(fmaxf(m0, acc0[qt][2]), acc0[qt][3]);
+                        m1 = fmaxf(fmaxf(m1, acc1[qt][0]), acc1[qt][1]);
+                        m1 = fmaxf(fmaxf(m1, acc1[qt][2]), acc1[qt][3]);
+                    }
+                    colm[tp & 3] = m0;
+                    colm[(tp & 3) + 1] = m1;
+                    if ((tp & 3) == 2) {
+                        // lanes: [tile tp-2 | tile tp-1] after the 32-swap, then 16-swap gives rows
+                        // [tile0, tile2, tile1, tile3] of the four tiles, full 64-row maxima.
+                        auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(colm[0]),
+                                                                    __float_as_uint(colm[1]), false, false);
+                        auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(colm[2]),
+                                                                    __float_as_uint(colm[3]), false, false);
+                        const float y01 = fmaxf(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
+                        const float y23 = fmaxf(__uint_as_float(s23[0]), __uint_as_float(s23[1]));
+                        auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(y01), __float_as_uint(y23),
+                                                                  false, false);
+                        const float z = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+                        const int trow = lane >> 4;
+                        const int tsel = ((trow & 1) << 1) | (trow >> 1);
+                        const int tile = grp * G + (tp - 2) + tsel;
+                        atomicMax(&colmax_lds[tile * TILE + c], fkey(z));
+                    }
+                }
+            }
+#pragma unroll
+            for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    gid[qt][r] = (nb[qt][r] > best[qt][r]) ? grp : gid[qt][r];
+                    best[qt][r] = nb[qt][r];
+                }
+        }
+
+        // ---- row flush: max over the 16 slots of each row, lowest (group, slot) among equals
+        uint64_t *rp = p.rowpart + pair * p.rowpart_bs + (long long)chunk_id * p.rowcap;
+#pragma unroll
+        for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float bv = best[qt][r];
+                const float m = row16_max(bv);
+                const uint32_t id = ((gbase + (uint32_t)gid[qt][r]) << 4) | (uint32_t)c;
+                const uint32_t cand = row16_min(bv == m ? id : 0xffffffffu);
+                const int row = row0 + qt * 16 + 4 * g + r;
+                if (c == 0 && row < nq) rp[row] = row_key(m, cand);
+            }
+    }
+
+    if constexpr (COLMAX) {
+        __syncthreads();
+        uint32_t *cp = p.colpart + pair * p.colpart_bs + (long long)qblk * p.nref + r0;
+        for (int s = tid; s < nslots; s += NW * 64) {
+            const int tile = s / TILE, slot = s % TILE;
+            const int r = (tile / G) * GROUP + slot * TILE + (tile % G);
+            if (r < nvalid) cp[r] = colmax_lds[s];
+        }
+    }
+}
+
+}  // namespace ddm

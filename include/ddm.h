@@ -1,0 +1,135 @@
+/*
+ * ddm.h -- C ABI of the MI355X (gfx950) dense descriptor matching library.
+ *
+ * What is computed (cited by page title and section):
+ *  - Descriptor maps: D1 in R^{H1 x W1 x d}, D2 in R^{H2 x W2 x d}, one d-vector
+ *    per pixel, unit L2 norm as produced by MASt3R's matching head ("MASt3R"
+ *    note on cv-learn.com, section 手法とアーキテクチャ, matching-head paragraph).
+ *  - NN_2(x): the pixel j of image 2 maximising the dot product <x, D2_j>, the
+ *    lowest j on exact ties; NN_1 likewise over image 1 (same note, FRM
+ *    paragraph, where NN is the nearest-neighbour function of the reciprocal set).
+ *  - Exhaustive reciprocal set M = {(i, j) : j = NN_2(D1_i) and i = NN_1(D2_j)}
+ *    (same note, FRM paragraph).
+ *  - Fast Reciprocal Matching: k seeds on a regular grid, NN round trips
+ *    U^t -> V^t -> U^{t+1}, keep the seeds whose trajectory cycles (same note,
+ *    FRM paragraph), run as the fast_reciprocal_NNs routine quoted in
+ *    "DUSt3R和MASt3R论文阅读" (Staskaer blog, section MASt3R matching): seed grid,
+ *    forward query, test against the previous image-2 pixel, backward query,
+ *    test against the previous image-1 pixel, at most max_iter iterations,
+ *    converged = no longer active, unique pairs sorted by the image-1 index.
+ *
+ * Conventions shared by every entry point:
+ *  - Maps are row-major [H][W][d] (pixel p = x + W*y, then d components),
+ *    contiguous, in device memory, 16-byte aligned (fp16/bf16) or 4-byte
+ *    aligned (fp32). Values must be finite. Element types: DDM_F32 (float),
+ *    DDM_F16 (IEEE binary16), DDM_BF16 (bfloat16); products are accumulated in
+ *    fp32 (fp16/bf16 products are exact in fp32).
+ *  - All device buffers (inputs, outputs, workspace) belong to the caller. The
+ *    library never allocates device memory; it asks for a workspace of the size
+ *    the matching *_workspace_bytes function returns and uses it as scratch.
+ *  - Calls only enqueue work on `stream` and return; outputs (including device
+ *    counts) are valid once the stream has reached that point.
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    leave every output untouched. Status codes are the ddm_status values; a HIP
+ *    launch failure is reported as DDM_ERR_HIP. Calls that share a workspace
+ *    must not overlap on the device.
+ *  - Scores are the fp32 dot products computed by the matrix cores.
+ *  - Limits: 1 <= d <= 128, H*W < 2^31 / 16 pixels per map.
+ */
+#ifndef DDM_H
+#define DDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DDM_F32 = 0, DDM_F16 = 1, DDM_BF16 = 2 } ddm_dtype;
+
+typedef enum {
+    DDM_OK = 0,
+    DDM_ERR_INVALID = -1,     /* null pointer, bad size, misaligned or bad parameter */
+    DDM_ERR_CAPACITY = -2,    /* output capacity below the largest possible result */
+    DDM_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
+    DDM_ERR_UNSUPPORTED = -4, /* dtype or d outside what the kernels handle */
+    DDM_ERR_HIP = -5          /* a HIP call failed while enqueueing */
+} ddm_status;
+
+#define DDM_MAX_D 128
+#define DDM_MAX_ITER 64
+
+/* Human-readable name of a status code (static string). */
+const char *ddm_status_str(int status);
+
+/* Number of grid seeds for an H x W image with stride S: the seed grid of the
+ * quoted fast_reciprocal_NNs routine, rows S/2, S/2+S, ... < H and columns
+ * S/2, S/2+S, ... < W. Returns -1 for S <= 0 or negative sizes. */
+int64_t ddm_seed_count(int H, int W, int grid_stride);
+
+/* ---------------------------------------------------------------- NN ----
+ * Brute-force nearest neighbour (argmax of the dot product, lowest index on
+ * exact ties) of M query rows against all N reference rows.
+ *   Q       [NQ][d] query map; query a is row q_rows[a] (or row a when q_rows
+ *           is NULL, which needs NQ >= M)
+ *   q_rows  device int32[M] with entries in [0, NQ), or NULL
+ *   R       [N][d] reference map
+ *   out_idx device int32[M]: NN index in [0, N)
+ *   out_score device float[M]: the fp32 dot product of the pair
+ */
+size_t ddm_nn_workspace_bytes(int NQ, int M, int N, int d, int dtype);
+int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, int N, int d, int dtype,
+           int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes,
+           hipStream_t stream);
+
+/* ---------------------------------------------------------------- FRM ---
+ * Fast Reciprocal Matching from the stride-`grid_stride` seed grid of image 1
+ * with at most `max_iter` iterations (1..DDM_MAX_ITER). Outputs are the unique
+ * converged pairs (i in image 1, j in image 2) as linear pixel indices,
+ * strictly ascending in i, with their fp32 scores:
+ *   out_i, out_j, out_score  device arrays of `capacity` entries;
+ *                            capacity >= ddm_seed_count(H1, W1, grid_stride)
+ *   out_count                device int32: number of pairs written
+ *   seed_state               device int32[k][4] or NULL: per seed (in grid
+ *                            order) u, v, iteration in which it converged
+ *                            (-1 if it did not), 0
+ *   query_counts             device int32[2*max_iter] or NULL: number of
+ *                            forward / backward NN queries in each iteration
+ *                            (entry 2t = forward, 2t+1 = backward of iteration t+1)
+ * k = 0 (stride larger than the image) is valid and yields 0 pairs. */
+size_t ddm_frm_workspace_bytes(int B, int H1, int W1, int H2, int W2, int d, int dtype,
+                               int grid_stride, int max_iter);
+int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                  int grid_stride, int max_iter,
+                  int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
+                  int32_t *seed_state, int32_t *query_counts,
+                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* B independent pairs in one call: D1 is [B][H1][W1][d], D2 is [B][H2][W2][d].
+ * Pair b writes its pairs at out_*[b * capacity ...] and its count at
+ * out_count[b]; seed_state is [B][k][4] and query_counts [B][2*max_iter].
+ * Each pair's result equals a single ddm_frm_match call on that pair. */
+int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d,
+                          int dtype, int grid_stride, int max_iter,
+                          int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
+                          int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------- mutual NN ---
+ * Exhaustive reciprocal nearest neighbours M (ascending in i), computed in a
+ * single pass over all N1 x N2 scores with row arg-max and column max fused.
+ *   capacity >= min(H1*W1, H2*W2); out_count as for FRM.
+ *   nn12, s12  device int32[N1] / float[N1] or NULL: NN_2 of every pixel of
+ *              image 1 and its score. */
+size_t ddm_mutual_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype);
+int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                  int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
+                  int32_t *nn12, float *s12,
+                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DDM_H */

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/ddm.h declares, and rejects bad arguments before
+enqueueing anything (so fake device pointers are never touched)."""
+import ctypes as C
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddm.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import dense_descriptor_matching_amd as ddm
+    if not os.path.exists(ddm.LIB_PATH):
+        pytest.fail("libddm.so not built: run __graft_entry__.build()")
+    return ddm.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in ddm.h but not exported"
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.ddm_status_str(code)
+    assert L.ddm_status_str(99) == b"unknown status"
+
+
+def test_seed_count_closed_forms(L):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "seed_grid.json")))
+    for c in g["cases"]:
+        assert L.ddm_seed_count(c["H"], c["W"], c["S"]) == c["k"]
+    assert L.ddm_seed_count(10, 10, 0) == -1
+
+
+def test_workspace_sizes(L):
+    assert L.ddm_frm_workspace_bytes(1, 512, 384, 512, 384, 24, 1, 8, 10) > 0
+    assert L.ddm_frm_workspace_bytes(16, 512, 384, 512, 384, 24, 1, 8, 10) > \
+        L.ddm_frm_workspace_bytes(1, 512, 384, 512, 384, 24, 1, 8, 10)
+    assert L.ddm_mutual_workspace_bytes(512, 384, 512, 384, 24, 1) > 0
+    assert L.ddm_nn_workspace_bytes(100, 100, 1000, 24, 1) > 0
+    # invalid requests report 0
+    assert L.ddm_frm_workspace_bytes(1, 512, 384, 512, 384, 0, 1, 8, 10) == 0
+    assert L.ddm_frm_workspace_bytes(1, 512, 384, 512, 384, 24, 9, 8, 10) == 0
+    assert L.ddm_frm_workspace_bytes(1, 512, 384, 512, 384, 24, 1, 8, 0) == 0
+    assert L.ddm_mutual_workspace_bytes(0, 384, 512, 384, 24, 1) == 0
+    assert L.ddm_nn_workspace_bytes(1, 1, 1, 129, 1) == 0
+
+
+FAKE = 1 << 40        # 16-byte aligned, never dereferenced: every case fails validation first
+
+
+def _frm(L, **kw):
+    a = dict(D1=FAKE, H1=64, W1=48, D2=FAKE, H2=64, W2=48, d=24, dtype=1, S=8, it=10, oi=FAKE, oj=FAKE, os=FAKE,
+             cap=48, cnt=FAKE, st=None, qc=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return L.ddm_frm_match(a["D1"], a["H1"], a["W1"], a["D2"], a["H2"], a["W2"], a["d"], a["dtype"], a["S"], a["it"],
+                           a["oi"], a["oj"], a["os"], a["cap"], a["cnt"], a["st"], a["qc"], a["ws"], a["wsb"], None)
+
+
+def test_frm_rejects_bad_arguments(L):
+    assert _frm(L, D1=None) == -1
+    assert _frm(L, D2=None) == -1
+    assert _frm(L, oi=None) == -1
+    assert _frm(L, cnt=None) == -1
+    assert _frm(L, H1=0) == -1
+    assert _frm(L, W2=-3) == -1
+    assert _frm(L, S=0) == -1
+    assert _frm(L, it=0) == -1
+    assert _frm(L, it=65) == -1
+    assert _frm(L, d=0) == -4
+    assert _frm(L, d=129) == -4
+    assert _frm(L, dtype=3) == -4
+    assert _frm(L, cap=47) == -2
+    assert _frm(L, ws=None) == -3
+    assert _frm(L, wsb=16) == -3
+    assert _frm(L, D1=FAKE + 2) == -1          # fp16 map not 16-byte aligned
+    assert _frm(L, D2=FAKE + 2, dtype=0) == -1          # fp32 map not 4-byte aligned
+
+
+def test_frm_batched_rejects_bad_batch(L):
+    r = L.ddm_frm_match_batched(0, FAKE, 64, 48, FAKE, 64, 48, 24, 1, 8, 10, FAKE, FAKE, FAKE, 48, FAKE, None,
+                                None, FAKE, 1 << 40, None)
+    assert r == -1
+
+
+def test_mutual_rejects_bad_arguments(L):
+    def m(**kw):
+        a = dict(D1=FAKE, D2=FAKE, d=24, dtype=1, cap=3072, ws=FAKE, wsb=1 << 40, nn=None, s=None)
+        a.update(kw)
+        return L.ddm_mutual_nn(a["D1"], 64, 48, a["D2"], 64, 48, a["d"], a["dtype"], FAKE, FAKE, FAKE, a["cap"],
+                               FAKE, a["nn"], a["s"], a["ws"], a["wsb"], None)
+    assert m(D1=None) == -1
+    assert m(cap=3071) == -2
+    assert m(wsb=0) == -3
+    assert m(dtype=5) == -4
+    assert m(nn=FAKE) == -1              # nn12 without s12
+
+
+def test_nn_rejects_bad_arguments(L):
+    def n(**kw):
+        a = dict(Q=FAKE, NQ=10, rows=None, M=10, R=FAKE, N=100, d=24, dtype=1, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return L.ddm_nn(a["Q"], a["NQ"], a["rows"], a["M"], a["R"], a["N"], a["d"], a["dtype"], FAKE, FAKE,
+                        a["ws"], a["wsb"], None)
+    assert n(M=0) == -1
+    assert n(N=0) == -1
+    assert n(NQ=5) == -1                 # identity queries need NQ >= M
+    assert n(R=None) == -1
+    assert n(wsb=8) == -3
+    assert n(d=200) == -4
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import dense_descriptor_matching_amd as ddm
+    x = torch.zeros(4, 4, 24, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        ddm.frm_match(x, x)
+    with pytest.raises(TypeError):
+        ddm.mutual_nn(x, x)
