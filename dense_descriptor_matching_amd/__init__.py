@@ -53,6 +53,8 @@ def _declare(lib):
     lib.ddm_mutual_workspace_bytes.argtypes = [I, I, I, I, I, I]; lib.ddm_mutual_workspace_bytes.restype = SZ
     lib.ddm_mutual_nn.argtypes = [P, I, I, P, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
     lib.ddm_mutual_nn.restype = I
+    lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
+    lib.ddm_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]; lib.ddm_profile_read.restype = I
     return lib
 
 
@@ -100,6 +102,18 @@ def seed_count(H: int, W: int, grid_stride: int) -> int:
 def to_xy(idx: torch.Tensor, W: int):
     """Linear pixel index -> (x, y)."""
     return idx % W, torch.div(idx, W, rounding_mode="floor")
+
+
+def profile_enable(mask: int):
+    """Bracket later sweep launches with HIP events (bit 0: mutual sweep, bit 1: NN/FRM sweeps)."""
+    _rc(lib().ddm_profile_enable(mask), "ddm_profile_enable")
+
+
+def profile_read():
+    """(summed sweep milliseconds, number of timed launches) since the last read."""
+    ms = C.c_double(0.0); n = C.c_int64(0)
+    _rc(lib().ddm_profile_read(C.byref(ms), C.byref(n)), "ddm_profile_read")
+    return ms.value, n.value
 
 
 # ------------------------------------------------------------------- NN
@@ -255,4 +269,4 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False):
 
 
 __all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "mutual_nn", "mutual_nn_into", "seed_count",
-           "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH"]
+           "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH", "profile_enable", "profile_read"]

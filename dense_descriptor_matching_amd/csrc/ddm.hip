@@ -8,6 +8,8 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 using namespace ddm;
 
@@ -98,7 +100,41 @@ hipError_t launch_sweep_dt(const MapFmt &f, const SweepArgs &a, dim3 grid, size_
     }
 }
 
+// ------------------------------------------------------------ sweep timing
+// When enabled, every sweep launch of the selected kinds is bracketed by two
+// HIP events on its stream; ddm_profile_read sums their elapsed times.
+struct Profiler {
+    std::mutex mu;
+    int mask = 0;                                   // 1 = mutual sweeps, 2 = NN/FRM sweeps
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending, pool;
+};
+Profiler &prof() { static Profiler p; return p; }
+
+hipError_t launch_sweep_impl(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s);
+
 hipError_t launch_sweep(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s) {
+    Profiler &P = prof();
+    const int kind = colmax ? 1 : 2;
+    if (!(P.mask & kind)) return launch_sweep_impl(f, colmax, a, grid, s);
+    std::pair<hipEvent_t, hipEvent_t> ev;
+    {
+        std::lock_guard<std::mutex> g(P.mu);
+        if (P.pool.empty()) {
+            if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess)
+                return hipErrorOutOfMemory;
+        } else {
+            ev = P.pool.back(); P.pool.pop_back();
+        }
+    }
+    hipError_t e = hipEventRecord(ev.first, s);
+    if (e == hipSuccess) e = launch_sweep_impl(f, colmax, a, grid, s);
+    if (e == hipSuccess) e = hipEventRecord(ev.second, s);
+    std::lock_guard<std::mutex> g(P.mu);
+    P.pending.push_back(ev);
+    return e;
+}
+
+hipError_t launch_sweep_impl(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s) {
     const size_t lds = sweep_lds(f, a.chunk, colmax);
     switch (f.dtype) {
     case DT_F16: return colmax ? launch_sweep_dt<DT_F16, true>(f, a, grid, lds, s)
@@ -372,6 +408,32 @@ const char *ddm_status_str(int status) {
 }
 
 int64_t ddm_seed_count(int H, int W, int grid_stride) { return seed_count(H, W, grid_stride); }
+
+int ddm_profile_enable(int mask) {
+    if (mask < 0 || mask > 3) return DDM_ERR_INVALID;
+    std::lock_guard<std::mutex> g(prof().mu);
+    prof().mask = mask;
+    return DDM_OK;
+}
+
+int ddm_profile_read(double *total_ms, int64_t *launches) {
+    if (!total_ms || !launches) return DDM_ERR_INVALID;
+    Profiler &P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    double sum = 0.0;
+    int64_t n = 0;
+    int rc = DDM_OK;
+    for (auto &ev : P.pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(ev.second) != hipSuccess || hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess)
+            rc = DDM_ERR_HIP;
+        sum += ms; ++n;
+        P.pool.push_back(ev);
+    }
+    P.pending.clear();
+    *total_ms = sum; *launches = n;
+    return rc;
+}
 
 }  // extern "C"
 

@@ -129,6 +129,16 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
                   int32_t *nn12, float *s12,
                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------- kernel timing ---
+ * Benchmark aid, off by default. ddm_profile_enable(mask) makes later calls
+ * bracket each fused NN sweep launch with two HIP events on the call's stream:
+ * mask bit 0 = the mutual-NN sweep, bit 1 = the NN / FRM sweeps, 0 = off (the
+ * library then creates no events). ddm_profile_read waits for the recorded
+ * events, returns the summed elapsed milliseconds and the number of launches,
+ * and forgets them. Events are created on first use and kept for reuse. */
+int ddm_profile_enable(int mask);
+int ddm_profile_read(double *total_ms, int64_t *launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,129 @@
+"""GPU parity at the five full-size workloads, in the launch configuration the
+benchmark times (rules in tests/parity.py).
+
+  tiny_frm_64x48x24_f32           full oracle
+  frm_512x384x24_f16              full oracle (all 3072 seeds), query counts too
+  mutual_512x384x24_f16           sampled rows: NN row by row, reciprocity of each
+  batched_frm_16x512x384x24_f16   batch == 16 single calls; oracle on sampled seeds
+  hard_frm_512x512x64_bf16        oracle on sampled seeds (trajectories are per seed)
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import TAU, check_frm, check_nn, exact_scores, near_reciprocal
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ddm():
+    import dense_descriptor_matching_amd as m
+    m.lib()
+    return m
+
+
+def dev(a, dtype):
+    from synth.torchio import to_device
+    return to_device(a, dtype, "cuda")
+
+
+def _frm_run(ddm, p, S, it):
+    i, j, s, st = ddm.frm_match(dev(p.D1, p.dtype), dev(p.D2, p.dtype), S, it, return_state=True)
+    return (i.cpu().numpy(), j.cpu().numpy(), s.cpu().numpy(), st["state"].cpu().numpy(),
+            st["query_counts"].cpu().numpy())
+
+
+def test_tiny_frm_full(ddm):
+    (p,) = synth.make_config("tiny_frm_64x48x24_f32")
+    i, j, s, st, qc = _frm_run(ddm, p, 8, 10)
+    A, B = oracle.decode(p.D1, p.dtype), oracle.decode(p.D2, p.dtype)
+    seeds = oracle.seed_grid(64, 48, 8)
+    assert len(seeds) == 48
+    amb, n = check_frm(A, B, st, i, j, s, seeds, 10, query_counts=qc)
+    assert len(i) > 30
+
+
+def test_frm_512x384_full(ddm):
+    (p,) = synth.make_config("frm_512x384x24_f16")
+    i, j, s, st, qc = _frm_run(ddm, p, 8, 10)
+    A, B = oracle.decode(p.D1, p.dtype), oracle.decode(p.D2, p.dtype)
+    seeds = oracle.seed_grid(512, 384, 8)
+    assert len(seeds) == 3072
+    amb, n = check_frm(A, B, st, i, j, s, seeds, 10, query_counts=qc)
+    print(f"pairs={len(i)} ambiguous seeds={amb} query counts={qc.tolist()}")
+    assert len(i) > 2500
+
+
+def test_mutual_512x384_sampled(ddm):
+    (p,) = synth.make_config("mutual_512x384x24_f16")
+    gi, gj, gs, nn12, s12 = ddm.mutual_nn(dev(p.D1, p.dtype), dev(p.D2, p.dtype), return_nn=True)
+    gi, gj, gs = gi.cpu().numpy(), gj.cpu().numpy(), gs.cpu().numpy()
+    nn12, s12 = nn12.cpu().numpy(), s12.cpu().numpy()
+    A, B = oracle.decode(p.D1, p.dtype), oracle.decode(p.D2, p.dtype)
+    N = 512 * 384
+    # whole-output properties
+    assert np.all(np.diff(gi) > 0) and len(gi) > 1000
+    assert np.array_equal(nn12[gi], gj) and np.array_equal(s12[gi], gs)
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([rng.choice(N, 320, replace=False), gi[rng.choice(len(gi), 64, replace=False)]]))
+    rows = rows.astype(np.int32)
+    check_nn(A, B, rows, nn12[rows], s12[rows])
+    o_j, s1, m1 = oracle.nn(A, B, qrows=rows)
+    back, s1c, mc = oracle.nn(B, A, qrows=o_j)
+    gpu = dict(zip(gi.tolist(), gj.tolist()))
+    n_mutual = 0
+    for r, oj, mr, bk, mcol in zip(rows.tolist(), o_j.tolist(), m1, back.tolist(), mc):
+        is_mutual = bk == r
+        n_mutual += is_mutual
+        if is_mutual and mr >= TAU and mcol >= TAU:
+            assert gpu.get(r) == oj, f"sharp reciprocal pair ({r}, {oj}) missing"
+        if r in gpu and not (is_mutual and gpu[r] == oj):
+            assert near_reciprocal(A, B, r, gpu[r]), f"GPU pair ({r}, {gpu[r]}) is not reciprocal"
+    assert n_mutual > 0
+    np.testing.assert_allclose(gs[:200], exact_scores(A, B, gi[:200], gj[:200]), atol=TAU, rtol=0)
+
+
+def test_batched_frm_16_pairs(ddm):
+    import torch
+    pairs = synth.make_config("batched_frm_16x512x384x24_f16")
+    D1 = torch.stack([dev(p.D1, p.dtype) for p in pairs]); D2 = torch.stack([dev(p.D2, p.dtype) for p in pairs])
+    out = ddm.frm_match_batched(D1, D2, 8, 10, return_state=True)
+    seeds = oracle.seed_grid(512, 384, 8)
+    rng = np.random.default_rng(7)
+    for b, p in enumerate(pairs):
+        i, j, s, st, qc = _frm_run(ddm, p, 8, 10)
+        bi, bj, bs, bst = out[b]
+        assert np.array_equal(i, bi.cpu().numpy()) and np.array_equal(j, bj.cpu().numpy())
+        assert np.array_equal(s, bs.cpu().numpy()) and np.array_equal(st, bst["state"].cpu().numpy())
+        assert np.array_equal(qc, bst["query_counts"].cpu().numpy())
+        if b in (0, 9):
+            A, B = oracle.decode(p.D1, p.dtype), oracle.decode(p.D2, p.dtype)
+            sel = np.sort(rng.choice(len(seeds), 96, replace=False))
+            check_frm(A, B, st, i, j, s, seeds, 10, seed_sel=sel)
+
+
+def test_hard_frm_512x512x64_bf16_sampled(ddm):
+    (p,) = synth.make_config("hard_frm_512x512x64_bf16")
+    i, j, s, st, qc = _frm_run(ddm, p, 4, 20)
+    A, B = oracle.decode(p.D1, p.dtype), oracle.decode(p.D2, p.dtype)
+    seeds = oracle.seed_grid(512, 512, 4)
+    assert len(seeds) == 16384
+    sel = np.sort(np.random.default_rng(11).choice(len(seeds), 48, replace=False))
+    amb, n = check_frm(A, B, st, i, j, s, seeds, 20, seed_sel=sel)
+    assert qc[0] == 16384 and qc[1] == 16384
+    print(f"pairs={len(i)} sampled ambiguous={amb}/{n} query counts={qc.tolist()}")
+
+
+def test_determinism_full_size(ddm):
+    import torch
+    (p,) = synth.make_config("frm_512x384x24_f16")
+    a = _frm_run(ddm, p, 8, 10); b = _frm_run(ddm, p, 8, 10)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    (q,) = synth.make_config("mutual_512x384x24_f16")
+    D1, D2 = dev(q.D1, q.dtype), dev(q.D2, q.dtype)
+    r1 = ddm.mutual_nn(D1, D2); r2 = ddm.mutual_nn(D1, D2)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
