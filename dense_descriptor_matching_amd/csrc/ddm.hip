@@ -15,13 +15,17 @@ using namespace ddm;
 
 namespace {
 
-// Default sweep shape: 4 waves x 8 query tiles = 512 query rows per sub-block.
-constexpr int RQ = 8;
-constexpr int NW = 4;
-constexpr int SB_ROWS = NW * RQ * 16;
-// fp32 maps: fewer query tiles so that up to 32 K-blocks of A fit in VGPRs.
-constexpr int RQ32 = 2;
-constexpr int SB_ROWS32 = NW * RQ32 * 16;
+// Sweep shapes. Each wave holds RQ query tiles of 16 rows. The mutual sweep keeps
+// one LDS-resident chunk per CU, so its workgroup carries 8 waves (two per SIMD)
+// to overlap one wave's matrix-core work with the other's epilogue; the NN/FRM
+// sweeps use 4-wave workgroups and several workgroups per CU.
+constexpr int NW_NN = 4;
+constexpr int NW_MUTUAL = 8;
+constexpr int nw_for(bool colmax) { return colmax ? NW_MUTUAL : NW_NN; }
+// Query tiles per wave: 6 for fp16/bf16 with up to 64 components (two
+// accumulator sets of the software pipeline fit in 256 VGPRs), 4 for wider
+// rows, 2 for fp32 maps (up to 32 K-blocks of A resident).
+constexpr int rq_for(int dt, int nkb) { return dt == DT_F32 ? 2 : (nkb <= 2 ? 6 : 4); }
 constexpr size_t LDS_MAX = 160 * 1024;
 constexpr int MAX_PIX = 1 << 27;
 
@@ -33,7 +37,8 @@ struct MapFmt {
     int esz;       // bytes per element
     bool repack;   // rows are copied into a zero-padded [n][ld] buffer first
     int tile_bytes() const { return dtype == DT_F32 ? ld * 16 * 4 : np * 16 * 16; }
-    int sb_rows() const { return dtype == DT_F32 ? SB_ROWS32 : SB_ROWS; }
+    int group() const { return TILE * group_tiles(dtype); }          // references per index group
+    int sb_rows(bool colmax) const { return nw_for(colmax) * rq_for(dtype, nkb) * 16; }
 };
 
 bool make_fmt(int dtype, int d, MapFmt *f) {
@@ -61,8 +66,9 @@ struct Bump {
 
 int chunk_limit(const MapFmt &f, bool colmax) {
     const size_t per_ref = (size_t)f.tile_bytes() / TILE + (colmax ? 4 : 0);
-    int c = (int)(LDS_MAX / per_ref) / GROUP * GROUP;
-    return std::max(c, GROUP);
+    const int grp = f.group();
+    int c = (int)(LDS_MAX / per_ref) / grp * grp;
+    return std::max(c, grp);
 }
 
 size_t sweep_lds(const MapFmt &f, int chunk, bool colmax) {
@@ -72,11 +78,17 @@ size_t sweep_lds(const MapFmt &f, int chunk, bool colmax) {
 // ----------------------------------------------------------------- dispatch
 template <int DT, int NP, int NKB, bool COLMAX>
 hipError_t launch_sweep_t(const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s) {
-    constexpr int rq = (DT == DT_F32) ? RQ32 : RQ;
-    auto k = sweep_kernel<DT, NP, NKB, rq, NW, COLMAX>;
-    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(NW * 64), lds, s, a);
+    constexpr int rq = rq_for(DT, NKB);
+    constexpr int nw = nw_for(COLMAX);
+    auto k = sweep_kernel<DT, NP, NKB, rq, nw, COLMAX>;
+    static bool attr_set = false;      // the attribute is set once per instantiation
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)LDS_MAX);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(k, grid, dim3(nw * 64), lds, s, a);
     return hipGetLastError();
 }
 
@@ -202,11 +214,11 @@ int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p) {
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
     if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
     p->NQ = NQ; p->M = M; p->N = N;
-    const int sbr = p->f.sb_rows();
+    const int sbr = p->f.sb_rows(false);
     p->qblocks = (M + sbr - 1) / sbr;
     int chunk = chunk_limit(p->f, false);
     // enough workgroups to fill the chip: shrink the chunk while fewer than 2048
-    while (chunk > GROUP && (long long)p->qblocks * ((N + chunk - 1) / chunk) < 2048) chunk -= GROUP;
+    while (chunk > p->f.group() && (long long)p->qblocks * ((N + chunk - 1) / chunk) < 2048) chunk -= p->f.group();
     p->chunk = chunk;
     p->nchunks = (N + chunk - 1) / chunk;
     Bump b;
@@ -229,7 +241,7 @@ struct FrmPlan {
 
 int frm_chunk(const MapFmt &f, int nref, long long wg_other) {
     int chunk = chunk_limit(f, false);
-    while (chunk > GROUP && wg_other * ((nref + chunk - 1) / chunk) < 2048) chunk -= GROUP;
+    while (chunk > f.group() && wg_other * ((nref + chunk - 1) / chunk) < 2048) chunk -= f.group();
     return chunk;
 }
 
@@ -242,7 +254,7 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
     p->S = S; p->max_iter = max_iter; p->nhalf = 2 * max_iter;
     p->k = (int)seed_count(H1, W1, S);
     p->kx = W1 > S / 2 ? (W1 - S / 2 + S - 1) / S : 0;
-    const int sbr = p->f.sb_rows();
+    const int sbr = p->f.sb_rows(false);
     const int kk = std::max(p->k, 1);
     p->qblocks = (kk + sbr - 1) / sbr;
     p->chunk2 = frm_chunk(p->f, p->N2, (long long)p->qblocks * B);
@@ -363,11 +375,11 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p)
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
     if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
     p->N1 = H1 * W1; p->N2 = H2 * W2;
-    const int sbr = p->f.sb_rows();
+    const int sbr = p->f.sb_rows(true);
     const int nsb = (p->N1 + sbr - 1) / sbr;
     int chunk = chunk_limit(p->f, true);
     // at least ~2 workgroups per CU along the chunk axis alone when the map is small
-    while (chunk > GROUP && (long long)nsb * ((p->N2 + chunk - 1) / chunk) < 512) chunk -= GROUP;
+    while (chunk > p->f.group() && (long long)nsb * ((p->N2 + chunk - 1) / chunk) < 512) chunk -= p->f.group();
     p->chunk = chunk;
     p->nchunks = (p->N2 + chunk - 1) / chunk;
     // query sub-blocks per workgroup: aim at ~2048 workgroups, fewer column partials

@@ -18,9 +18,10 @@ namespace ddm {
 // ---------------------------------------------------------------------------
 // Index resolution. A query's row partials (one per reference chunk) hold the
 // maximum score and the (group, slot) that produced it; the exact reference
-// is one of the 16 consecutive references group*256 + slot*16 + t. Sixteen
-// lanes recompute those dots (fp32 FMA on the stored values) and keep the
-// largest, lowest t on ties. The reported score is the matrix-core maximum.
+// is one of the G consecutive references group*GROUP + slot*G + t. Sixteen
+// lanes recompute those dots (fp32 FMA on the stored values, G/16 each) and
+// keep the largest, lowest t on ties. The reported score is the matrix-core
+// maximum.
 // ---------------------------------------------------------------------------
 template <int DT>
 __device__ __forceinline__ float dot_rows(const unsigned char *a, const unsigned char *b, int d) {
@@ -35,6 +36,7 @@ __device__ __forceinline__ void resolve_one(const uint64_t *part, int nchunks, l
                                             const unsigned char *qp, const unsigned char *R, int nref, int ld,
                                             int d, int sub, int *j_out, float *s_out) {
     constexpr int ESZ = Tr<DT>::ESZ;
+    constexpr int G = group_tiles(DT), GROUP = TILE * G;
     uint64_t k = 0;
     for (int ch = sub; ch < nchunks; ch += 16) {
         const uint64_t v = part[(long long)ch * rowcap + x];
@@ -47,10 +49,17 @@ __device__ __forceinline__ void resolve_one(const uint64_t *part, int nchunks, l
     }
     const float mval = fkey_inv((uint32_t)(k >> 32));
     const uint32_t id = ~(uint32_t)k;
-    const int j = (int)((id >> 4) * GROUP + (id & 15u) * TILE) + sub;
+    const int j0 = (int)((id >> 4) * GROUP + (id & 15u) * G);
     float s = -INFINITY;
-    if (j < nref) s = dot_rows<DT>(qp, R + (long long)j * ld * ESZ, d);
-    int bj = j < nref ? j : 0x7fffffff;
+    int bj = 0x7fffffff;
+#pragma unroll
+    for (int t = sub; t < G; t += 16) {          // ascending t: strict > keeps the lowest
+        const int j = j0 + t;
+        if (j < nref) {
+            const float v = dot_rows<DT>(qp, R + (long long)j * ld * ESZ, d);
+            if (v > s || bj == 0x7fffffff) { s = v; bj = j; }
+        }
+    }
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) {
         const float os = __shfl_xor(s, m, 16);

@@ -19,17 +19,16 @@
 // Epilogue (the part that bounds this kernel at d = 24)
 //   MFMA output lane l holds reference slot c = l % 16 and query rows
 //   4*(l/16) + r, r = 0..3. Row direction: per register a running maximum over
-//   a group of G = 16 tiles with one v_max3_f32 per two scores, then one
+//   a group of G = 32 tiles with one v_max3_f32 per two scores, then one
 //   compare + select per register and group to remember which group held the
-//   maximum (lazy index). Inside a group the 256 references are laid out so
-//   that slot c of tile t is reference 16*c + t: the 16 candidates of one
+//   maximum (lazy index). Inside a group the 512 references are laid out so
+//   that slot c of tile t is reference 32*c + t: the 32 candidates of one
 //   (group, slot) are contiguous, and (group, slot, t) order equals reference
 //   order, so the lowest-index tie-break survives. The exact index inside the
-//   group is recovered later by recomputing 16 candidate dots (ddm_resolve).
-//   Column direction (COLMAX): in-lane v_max3 chain over the wave's rows, two
-//   lane swaps (v_permlane32_swap, v_permlane16_swap) pack four tiles' column
-//   maxima into one register, one ds_max_u32 of order-preserving keys per four
-//   tiles into an LDS column array, flushed once per workgroup.
+//   group is recovered later by recomputing 32 candidate dots (resolve_one).
+//   Column direction (COLMAX): in-lane v_max3 chain over the wave's rows, then
+//   one ds_max_f32 per tile into an LDS column array (the four lanes that hold
+//   one column meet there), flushed once per workgroup as order-preserving keys.
 //
 // Invalid reference slots (chunk tail) hold NaN, whose scores are NaN and are
 // ignored by v_max3 (maxNum semantics); invalid query rows duplicate the last
@@ -43,8 +42,9 @@ namespace ddm {
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 constexpr int TILE = 16;            // references per MFMA tile
-constexpr int G = 16;               // tiles per index group
-constexpr int GROUP = TILE * G;     // references per index group
+// Tiles per index group: 32 for fp16/bf16 maps; 8 for fp32 maps, whose wider
+// rows would otherwise not fit one group of up to 128 components in LDS.
+constexpr int group_tiles(int dt) { return dt == 0 ? 8 : 32; }
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -158,6 +158,7 @@ template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
 __global__ void __launch_bounds__(NW * 64)
 sweep_kernel(SweepArgs p)
 {
+    constexpr int G = group_tiles(DT), GROUP = TILE * G;
     using T = Tr<DT>;
     using raw = typename T::raw;
     constexpr int E = T::E, PS = T::PS, ESZ = T::ESZ;
@@ -184,7 +185,7 @@ sweep_kernel(SweepArgs p)
     const int ngroups = (nvalid + GROUP - 1) / GROUP;
     const int nslots = ngroups * GROUP;
 
-    // ---- stage the chunk in LDS: slot c of tile t of group q <- reference q*256 + 16*c + t
+    // ---- stage the chunk in LDS: slot c of tile t of group q <- reference q*GROUP + G*c + t
     for (int qq = tid; qq < nslots * np; qq += NW * 64) {
         const int r = qq / np, pc = qq - r * np;
         raw v;
@@ -193,13 +194,13 @@ sweep_kernel(SweepArgs p)
         else
             v = T::nan_piece();
         const int grp = r / GROUP, w = r % GROUP;
-        const int tile = grp * G + (w % TILE);
-        const int c = w / TILE;
+        const int tile = grp * G + (w % G);
+        const int c = w / G;
         *reinterpret_cast<raw *>(lds + tile * TB + pc * 16 * PS + c * PS) = v;
     }
-    uint32_t *colmax_lds = reinterpret_cast<uint32_t *>(lds + (size_t)(p.chunk / TILE) * TB);
+    float *colmax_lds = reinterpret_cast<float *>(lds + (size_t)(p.chunk / TILE) * TB);
     if constexpr (COLMAX) {
-        for (int s = tid; s < nslots; s += NW * 64) colmax_lds[s] = 0u;
+        for (int s = tid; s < nslots; s += NW * 64) colmax_lds[s] = -INFINITY;
     }
     __syncthreads();
 
@@ -229,87 +230,140 @@ sweep_kernel(SweepArgs p)
             }
         }
 
-        float best[RQ][4];
+        // Running row state lives in two register sets that swap roles every
+        // group, so no copies are needed between groups.
+        float bA[RQ][4], bB[RQ][4];
         int gid[RQ][4];
 #pragma unroll
         for (int qt = 0; qt < RQ; ++qt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) { best[qt][r] = -INFINITY; gid[qt][r] = 0; }
+            for (int r = 0; r < 4; ++r) { bA[qt][r] = -INFINITY; gid[qt][r] = 0; }
 
-        for (int grp = 0; grp < ngroups; ++grp) {
-            const unsigned char *gb = lds + grp * G * TB;
-            float nb[RQ][4];
+        // ---- per tile pair: B fragments from LDS, MFMAs, epilogue
+        auto load_pair = [&](int tile, raw (&b0)[NKB], raw (&b1)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int qt = 0; qt < RQ; ++qt)
+            for (int kb = 0; kb < NKB; ++kb) {
+                b0[kb] = *reinterpret_cast<const raw *>(lds + tile * TB + boff[kb]);
+                b1[kb] = *reinterpret_cast<const raw *>(lds + (tile + 1) * TB + boff[kb]);
+            }
+        };
+        auto mma_pair = [&](const raw (&b0)[NKB], const raw (&b1)[NKB], f32x4_t (&c0)[RQ],
+                            f32x4_t (&c1)[RQ]) __attribute__((always_inline)) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) nb[qt][r] = best[qt][r];
-            float colm[4];
-#pragma unroll
-            for (int tp = 0; tp < G; tp += 2) {
-                raw b0[NKB], b1[NKB];
+            for (int qt = 0; qt < RQ; ++qt) {
+                c0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                c1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    b0[kb] = *reinterpret_cast<const raw *>(gb + tp * TB + boff[kb]);
-                    b1[kb] = *reinterpret_cast<const raw *>(gb + (tp + 1) * TB + boff[kb]);
-                }
-                f32x4_t acc0[RQ], acc1[RQ];
-#pragma unroll
-                for (int qt = 0; qt < RQ; ++qt) {
-                    acc0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    acc1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        if (NP > 0 || kb < nkb) {
-                            acc0[qt] = T::mma(a[qt][kb], b0[kb], acc0[qt]);
-                            acc1[qt] = T::mma(a[qt][kb], b1[kb], acc1[qt]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int qt = 0; qt < RQ; ++qt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        nb[qt][r] = fmaxf(fmaxf(nb[qt][r], acc0[qt][r]), acc1[qt][r]);
-                if constexpr (COLMAX) {
-                    float m0 = fmaxf(acc0[0][0], acc0[0][1]);
-                    float m1 = fmaxf(acc1[0][0], acc1[0][1]);
-                    m0 = fmaxf(fmaxf(m0, acc0[0][2]), acc0[0][3]);
-                    m1 = fmaxf(fmaxf(m1, acc1[0][2]), acc1[0][3]);
-#pragma unroll
-                    for (int qt = 1; qt < RQ; ++qt) {
-                        m0 = fmaxf(fmaxf(m0, acc0[qt][0]), acc0[qt][1]);
-                        m0 = fmaxf(fmaxf(m0, acc0[qt][2]), acc0[qt][3]);
-                        m1 = fmaxf(fmaxf(m1, acc1[qt][0]), acc1[qt][1]);
-                        m1 = fmaxf(fmaxf(m1, acc1[qt][2]), acc1[qt][3]);
-                    }
-                    colm[tp & 3] = m0;
-                    colm[(tp & 3) + 1] = m1;
-                    if ((tp & 3) == 2) {
-                        // lanes: [tile tp-2 | tile tp-1] after the 32-swap, then 16-swap gives rows
-                        // [tile0, tile2, tile1, tile3] of the four tiles, full 64-row maxima.
-                        auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(colm[0]),
-                                                                    __float_as_uint(colm[1]), false, false);
-                        auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(colm[2]),
-                                                                    __float_as_uint(colm[3]), false, false);
-                        const float y01 = fmaxf(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
-                        const float y23 = fmaxf(__uint_as_float(s23[0]), __uint_as_float(s23[1]));
-                        auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(y01), __float_as_uint(y23),
-                                                                  false, false);
-                        const float z = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-                        const int trow = lane >> 4;
-                        const int tsel = ((trow & 1) << 1) | (trow >> 1);
-                        const int tile = grp * G + (tp - 2) + tsel;
-                        atomicMax(&colmax_lds[tile * TILE + c], fkey(z));
+                    if (NP > 0 || kb < nkb) {
+                        c0[qt] = T::mma(a[qt][kb], b0[kb], c0[qt]);
+                        c1[qt] = T::mma(a[qt][kb], b1[kb], c1[qt]);
                     }
                 }
             }
+        };
+        // Row state: running maximum of each (row, slot) over the group's tiles,
+        // v_max3 consumes one score of each tile of the pair. Columns: in-lane
+        // maximum over the wave's rows, one LDS float-max per tile (the four
+        // lanes of a column, one per row group, meet in LDS).
+        auto epi_pair = [&](const f32x4_t (&c0)[RQ], const f32x4_t (&c1)[RQ], int tile, bool first,
+                            float (&bin)[RQ][4], float (&bout)[RQ][4]) __attribute__((always_inline)) {
 #pragma unroll
             for (int qt = 0; qt < RQ; ++qt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    gid[qt][r] = (nb[qt][r] > best[qt][r]) ? grp : gid[qt][r];
-                    best[qt][r] = nb[qt][r];
+                for (int r = 0; r < 4; ++r)
+                    bout[qt][r] = fmaxf(fmaxf(first ? bin[qt][r] : bout[qt][r], c0[qt][r]), c1[qt][r]);
+            if constexpr (COLMAX) {
+                float m0 = fmaxf(c0[0][0], c0[0][1]);
+                float m1 = fmaxf(c1[0][0], c1[0][1]);
+                m0 = fmaxf(fmaxf(m0, c0[0][2]), c0[0][3]);
+                m1 = fmaxf(fmaxf(m1, c1[0][2]), c1[0][3]);
+#pragma unroll
+                for (int qt = 1; qt < RQ; ++qt) {
+                    m0 = fmaxf(fmaxf(m0, c0[qt][0]), c0[qt][1]);
+                    m0 = fmaxf(fmaxf(m0, c0[qt][2]), c0[qt][3]);
+                    m1 = fmaxf(fmaxf(m1, c1[qt][0]), c1[qt][1]);
+                    m1 = fmaxf(fmaxf(m1, c1[qt][2]), c1[qt][3]);
                 }
+                float *cm = colmax_lds + tile * TILE + c;
+                __hip_atomic_fetch_max(cm, m0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_max(cm + TILE, m1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        };
+        auto mark = [&](int grp, float (&bin)[RQ][4], float (&bout)[RQ][4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gid[qt][r] = (bout[qt][r] > bin[qt][r]) ? grp : gid[qt][r];
+        };
+
+        if constexpr (DT == DT_F32) {
+            // fp32 maps (narrow K blocks, small maps): plain loop, tile loop kept rolled
+            for (int grp = 0; grp < ngroups; ++grp) {
+                for (int tp = 0; tp < G; tp += 2) {
+                    raw b0[NKB], b1[NKB];
+                    f32x4_t c0[RQ], c1[RQ];
+                    load_pair(grp * G + tp, b0, b1);
+                    mma_pair(b0, b1, c0, c1);
+                    epi_pair(c0, c1, grp * G + tp, tp == 0, bA, bB);
+                }
+                mark(grp, bA, bB);
+#pragma unroll
+                for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) bA[qt][r] = bB[qt][r];
+            }
+        } else {
+            // Software pipeline over tile pairs: the next pair's B fragments and
+            // MFMAs are issued before the current pair's epilogue, so the matrix
+            // cores work while the VALU reduces. Two accumulator sets alternate;
+            // the row state alternates between bA and bB every group.
+            const int last_tile = ngroups * G - 2;
+            raw b0[NKB], b1[NKB];
+            f32x4_t xA0[RQ], xA1[RQ], xB0[RQ], xB1[RQ];
+            load_pair(0, b0, b1);
+            mma_pair(b0, b1, xA0, xA1);
+            int grp = 0;
+            for (; grp + 1 < ngroups; grp += 2) {
+#pragma unroll
+                for (int q = 0; q < G; ++q) {
+                    const int tile = grp * G + 2 * q;
+                    const int ntile = min(tile + 2, last_tile);
+                    const bool second = q >= G / 2;
+                    load_pair(ntile, b0, b1);
+                    if (q % 2 == 0) {
+                        mma_pair(b0, b1, xB0, xB1);
+                        if (!second) epi_pair(xA0, xA1, tile, q == 0, bA, bB);
+                        else epi_pair(xA0, xA1, tile, q == G / 2, bB, bA);
+                    } else {
+                        mma_pair(b0, b1, xA0, xA1);
+                        if (!second) epi_pair(xB0, xB1, tile, false, bA, bB);
+                        else epi_pair(xB0, xB1, tile, false, bB, bA);
+                    }
+                    if (q == G / 2 - 1) mark(grp, bA, bB);
+                    if (q == G - 1) mark(grp + 1, bB, bA);
+                }
+            }
+            if (grp < ngroups) {
+#pragma unroll
+                for (int q = 0; q < G / 2; ++q) {
+                    const int tile = grp * G + 2 * q;
+                    const int ntile = min(tile + 2, last_tile);
+                    load_pair(ntile, b0, b1);
+                    if (q % 2 == 0) {
+                        mma_pair(b0, b1, xB0, xB1);
+                        epi_pair(xA0, xA1, tile, q == 0, bA, bB);
+                    } else {
+                        mma_pair(b0, b1, xA0, xA1);
+                        epi_pair(xB0, xB1, tile, false, bA, bB);
+                    }
+                }
+                mark(grp, bA, bB);
+#pragma unroll
+                for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) bA[qt][r] = bB[qt][r];
+            }
         }
 
         // ---- row flush: max over the 16 slots of each row, lowest (group, slot) among equals
@@ -318,7 +372,7 @@ sweep_kernel(SweepArgs p)
         for (int qt = 0; qt < RQ; ++qt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float bv = best[qt][r];
+                const float bv = bA[qt][r];
                 const float m = row16_max(bv);
                 const uint32_t id = ((gbase + (uint32_t)gid[qt][r]) << 4) | (uint32_t)c;
                 const uint32_t cand = row16_min(bv == m ? id : 0xffffffffu);
@@ -332,8 +386,8 @@ sweep_kernel(SweepArgs p)
         uint32_t *cp = p.colpart + pair * p.colpart_bs + (long long)qblk * p.nref + r0;
         for (int s = tid; s < nslots; s += NW * 64) {
             const int tile = s / TILE, slot = s % TILE;
-            const int r = (tile / G) * GROUP + slot * TILE + (tile % G);
-            if (r < nvalid) cp[r] = colmax_lds[s];
+            const int r = (tile / G) * GROUP + slot * G + (tile % G);
+            if (r < nvalid) cp[r] = fkey(colmax_lds[s]);
         }
     }
 }

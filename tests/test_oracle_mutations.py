@@ -8,6 +8,7 @@ mutation; the unmodified source must pass them all.
 """
 import os
 import subprocess
+import sys
 
 import pytest
 
@@ -72,7 +73,8 @@ def _build(src_text, out_dir, name):
     return so_path
 
 
-def _failures(so_path):
+def count_failures(so_path):
+    """Run every pin against one oracle build; returns how many fail."""
     failed = 0
     with oracle.use_library(so_path):
         for pin in PINS:
@@ -81,6 +83,26 @@ def _failures(so_path):
             except (AssertionError, IndexError, ValueError, MemoryError):
                 failed += 1
     return failed
+
+
+_RUNNER = """
+import sys
+sys.path[:0] = sys.argv[2:]
+import test_oracle_mutations as M
+sys.exit(min(M.count_failures(sys.argv[1]), 100))
+"""
+
+
+def _failures(so_path):
+    # A mutant may read or write out of bounds and crash; run it in its own
+    # process. A crash counts as a failed pin (the mistake was noticed).
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    r = subprocess.run([sys.executable, "-c", _RUNNER, so_path, here, root], capture_output=True, text=True,
+                       timeout=600)
+    if r.returncode < 0 or r.returncode > 100:
+        return 1
+    return r.returncode
 
 
 def test_unmodified_source_passes_all_pins(tmp_path):
