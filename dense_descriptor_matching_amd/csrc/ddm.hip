@@ -8,6 +8,8 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <array>
+#include <list>
 #include <mutex>
 #include <vector>
 
@@ -15,18 +17,16 @@ using namespace ddm;
 
 namespace {
 
-// Sweep shapes. Each wave holds RQ query tiles of 16 rows. The mutual sweep keeps
-// one LDS-resident chunk per CU, so its workgroup carries 8 waves (two per SIMD)
-// to overlap one wave's matrix-core work with the other's epilogue; the NN/FRM
-// sweeps use 4-wave workgroups and several workgroups per CU.
-constexpr int NW_NN = 4;
-constexpr int NW_MUTUAL = 8;
-constexpr int nw_for(bool colmax) { return colmax ? NW_MUTUAL : NW_NN; }
+// Sweep shapes. Each wave holds RQ query tiles of 16 rows. A workgroup keeps one
+// LDS-resident reference chunk and carries 8 waves (two per SIMD), so that one
+// wave's matrix-core work overlaps the other's epilogue; fp32 maps use 4 waves.
+constexpr int nw_for(int dt) { return dt == DT_F32 ? 4 : 8; }
 // Query tiles per wave: 6 for fp16/bf16 with up to 64 components (two
 // accumulator sets of the software pipeline fit in 256 VGPRs), 4 for wider
 // rows, 2 for fp32 maps (up to 32 K-blocks of A resident).
 constexpr int rq_for(int dt, int nkb) { return dt == DT_F32 ? 2 : (nkb <= 2 ? 6 : 4); }
 constexpr size_t LDS_MAX = 160 * 1024;
+constexpr long long MIN_WG = 256;          // one workgroup per CU
 constexpr int MAX_PIX = 1 << 27;
 
 struct MapFmt {
@@ -38,7 +38,7 @@ struct MapFmt {
     bool repack;   // rows are copied into a zero-padded [n][ld] buffer first
     int tile_bytes() const { return dtype == DT_F32 ? ld * 16 * 4 : np * 16 * 16; }
     int group() const { return TILE * group_tiles(dtype); }          // references per index group
-    int sb_rows(bool colmax) const { return nw_for(colmax) * rq_for(dtype, nkb) * 16; }
+    int sb_rows() const { return nw_for(dtype) * rq_for(dtype, nkb) * 16; }
 };
 
 bool make_fmt(int dtype, int d, MapFmt *f) {
@@ -76,40 +76,68 @@ size_t sweep_lds(const MapFmt &f, int chunk, bool colmax) {
 }
 
 // ----------------------------------------------------------------- dispatch
+// launch == false only raises the instantiation's dynamic-LDS limit (done once,
+// before any launch, so that it never happens inside a stream capture).
 template <int DT, int NP, int NKB, bool COLMAX>
-hipError_t launch_sweep_t(const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+hipError_t launch_sweep_t(const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s, bool launch) {
     constexpr int rq = rq_for(DT, NKB);
-    constexpr int nw = nw_for(COLMAX);
+    constexpr int nw = nw_for(DT);
     auto k = sweep_kernel<DT, NP, NKB, rq, nw, COLMAX>;
-    static bool attr_set = false;      // the attribute is set once per instantiation
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)LDS_MAX);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    if (!launch)
+        return hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_MAX);
     hipLaunchKernelGGL(k, grid, dim3(nw * 64), lds, s, a);
     return hipGetLastError();
 }
 
 template <int DT, bool COLMAX>
-hipError_t launch_sweep_dt(const MapFmt &f, const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+hipError_t launch_sweep_dt(const MapFmt &f, const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s, bool launch) {
     if constexpr (DT == DT_F32) {
-        if (f.nkb == 8) return launch_sweep_t<DT_F32, 0, 8, COLMAX>(a, grid, lds, s);
-        return launch_sweep_t<DT_F32, 0, 32, COLMAX>(a, grid, lds, s);
+        if (f.nkb == 8) return launch_sweep_t<DT_F32, 0, 8, COLMAX>(a, grid, lds, s, launch);
+        return launch_sweep_t<DT_F32, 0, 32, COLMAX>(a, grid, lds, s, launch);
     } else {
         switch (f.np) {
-        case 1: return launch_sweep_t<DT, 1, 1, COLMAX>(a, grid, lds, s);
-        case 2: return launch_sweep_t<DT, 2, 1, COLMAX>(a, grid, lds, s);
-        case 3: return launch_sweep_t<DT, 3, 1, COLMAX>(a, grid, lds, s);
-        case 4: return launch_sweep_t<DT, 4, 1, COLMAX>(a, grid, lds, s);
-        case 6: return launch_sweep_t<DT, 6, 2, COLMAX>(a, grid, lds, s);
-        case 8: return launch_sweep_t<DT, 8, 2, COLMAX>(a, grid, lds, s);
-        case 12: return launch_sweep_t<DT, 12, 3, COLMAX>(a, grid, lds, s);
-        case 16: return launch_sweep_t<DT, 16, 4, COLMAX>(a, grid, lds, s);
+        case 1: return launch_sweep_t<DT, 1, 1, COLMAX>(a, grid, lds, s, launch);
+        case 2: return launch_sweep_t<DT, 2, 1, COLMAX>(a, grid, lds, s, launch);
+        case 3: return launch_sweep_t<DT, 3, 1, COLMAX>(a, grid, lds, s, launch);
+        case 4: return launch_sweep_t<DT, 4, 1, COLMAX>(a, grid, lds, s, launch);
+        case 6: return launch_sweep_t<DT, 6, 2, COLMAX>(a, grid, lds, s, launch);
+        case 8: return launch_sweep_t<DT, 8, 2, COLMAX>(a, grid, lds, s, launch);
+        case 12: return launch_sweep_t<DT, 12, 3, COLMAX>(a, grid, lds, s, launch);
+        case 16: return launch_sweep_t<DT, 16, 4, COLMAX>(a, grid, lds, s, launch);
         default: return hipErrorInvalidValue;
         }
     }
+}
+
+hipError_t sweep_switch(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, size_t lds, hipStream_t s,
+                        bool launch) {
+    switch (f.dtype) {
+    case DT_F16: return colmax ? launch_sweep_dt<DT_F16, true>(f, a, grid, lds, s, launch)
+                               : launch_sweep_dt<DT_F16, false>(f, a, grid, lds, s, launch);
+    case DT_BF16: return colmax ? launch_sweep_dt<DT_BF16, true>(f, a, grid, lds, s, launch)
+                                : launch_sweep_dt<DT_BF16, false>(f, a, grid, lds, s, launch);
+    default: return colmax ? launch_sweep_dt<DT_F32, true>(f, a, grid, lds, s, launch)
+                           : launch_sweep_dt<DT_F32, false>(f, a, grid, lds, s, launch);
+    }
+}
+
+// Raise the dynamic-LDS limit of every sweep instantiation once per process.
+hipError_t prepare_kernels() {
+    static std::once_flag once;
+    static hipError_t status = hipSuccess;
+    std::call_once(once, [] {
+        const int dts[] = {DT_F32, DT_F16, DT_BF16};
+        for (int dt : dts)
+            for (int np : {1, 2, 3, 4, 6, 8, 12, 16})
+                for (int cm = 0; cm < 2; ++cm) {
+                    MapFmt f;
+                    if (!make_fmt(dt, dt == DT_F32 ? (np <= 4 ? 8 : 64) : np * 8, &f)) continue;
+                    SweepArgs a{};
+                    hipError_t e = sweep_switch(f, cm != 0, a, dim3(1), 0, nullptr, false);
+                    if (e != hipSuccess) status = e;
+                }
+    });
+    return status;
 }
 
 // ------------------------------------------------------------ sweep timing
@@ -147,15 +175,7 @@ hipError_t launch_sweep(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 g
 }
 
 hipError_t launch_sweep_impl(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s) {
-    const size_t lds = sweep_lds(f, a.chunk, colmax);
-    switch (f.dtype) {
-    case DT_F16: return colmax ? launch_sweep_dt<DT_F16, true>(f, a, grid, lds, s)
-                               : launch_sweep_dt<DT_F16, false>(f, a, grid, lds, s);
-    case DT_BF16: return colmax ? launch_sweep_dt<DT_BF16, true>(f, a, grid, lds, s)
-                                : launch_sweep_dt<DT_BF16, false>(f, a, grid, lds, s);
-    default: return colmax ? launch_sweep_dt<DT_F32, true>(f, a, grid, lds, s)
-                           : launch_sweep_dt<DT_F32, false>(f, a, grid, lds, s);
-    }
+    return sweep_switch(f, colmax, a, grid, sweep_lds(f, a.chunk, colmax), s, true);
 }
 
 #define DDM_DT_SWITCH(dtype, KERNEL, ...)                                                         \
@@ -214,11 +234,11 @@ int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p) {
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
     if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
     p->NQ = NQ; p->M = M; p->N = N;
-    const int sbr = p->f.sb_rows(false);
+    const int sbr = p->f.sb_rows();
     p->qblocks = (M + sbr - 1) / sbr;
     int chunk = chunk_limit(p->f, false);
-    // enough workgroups to fill the chip: shrink the chunk while fewer than 2048
-    while (chunk > p->f.group() && (long long)p->qblocks * ((N + chunk - 1) / chunk) < 2048) chunk -= p->f.group();
+    // largest LDS-resident chunk; shrink only while there is less than one workgroup per CU
+    while (chunk > p->f.group() && (long long)p->qblocks * ((N + chunk - 1) / chunk) < MIN_WG) chunk -= p->f.group();
     p->chunk = chunk;
     p->nchunks = (N + chunk - 1) / chunk;
     Bump b;
@@ -241,7 +261,7 @@ struct FrmPlan {
 
 int frm_chunk(const MapFmt &f, int nref, long long wg_other) {
     int chunk = chunk_limit(f, false);
-    while (chunk > f.group() && wg_other * ((nref + chunk - 1) / chunk) < 2048) chunk -= f.group();
+    while (chunk > f.group() && wg_other * ((nref + chunk - 1) / chunk) < MIN_WG) chunk -= f.group();
     return chunk;
 }
 
@@ -254,7 +274,7 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
     p->S = S; p->max_iter = max_iter; p->nhalf = 2 * max_iter;
     p->k = (int)seed_count(H1, W1, S);
     p->kx = W1 > S / 2 ? (W1 - S / 2 + S - 1) / S : 0;
-    const int sbr = p->f.sb_rows(false);
+    const int sbr = p->f.sb_rows();
     const int kk = std::max(p->k, 1);
     p->qblocks = (kk + sbr - 1) / sbr;
     p->chunk2 = frm_chunk(p->f, p->N2, (long long)p->qblocks * B);
@@ -375,7 +395,7 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p)
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
     if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
     p->N1 = H1 * W1; p->N2 = H2 * W2;
-    const int sbr = p->f.sb_rows(true);
+    const int sbr = p->f.sb_rows();
     const int nsb = (p->N1 + sbr - 1) / sbr;
     int chunk = chunk_limit(p->f, true);
     // at least ~2 workgroups per CU along the chunk axis alone when the map is small
@@ -399,6 +419,56 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p)
     p->o_r2 = p->f.repack ? b.take((size_t)p->N2 * p->f.ld * 2) : 0;
     p->total = b.off;
     return DDM_OK;
+}
+
+// ---------------------------------------------------------- graph replay
+// An FRM call is ~4*max_iter small launches whose host-side enqueue cost
+// exceeds their GPU time once the active set has shrunk. The sequence depends
+// only on the call's arguments, so it is captured once into a HIP graph on a
+// private capture stream, instantiated, cached (a few entries, most recently
+// used first) and replayed on the caller's stream with a single launch.
+using GraphKey = std::array<uint64_t, 24>;
+
+struct GraphCache {
+    std::mutex mu;
+    std::list<std::pair<GraphKey, hipGraphExec_t>> lru;
+    hipStream_t cap = nullptr;
+    static constexpr size_t kMax = 8;
+};
+GraphCache &graphs() { static GraphCache g; return g; }
+
+template <class Enqueue>
+int run_graphed(const GraphKey &key, hipStream_t stream, Enqueue enqueue) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return DDM_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone || (prof().mask & 2)) return enqueue(stream);   // direct launches
+    GraphCache &G = graphs();
+    std::lock_guard<std::mutex> lock(G.mu);
+    for (auto it = G.lru.begin(); it != G.lru.end(); ++it) {
+        if (it->first == key) {
+            G.lru.splice(G.lru.begin(), G.lru, it);
+            return hipGraphLaunch(G.lru.front().second, stream) == hipSuccess ? DDM_OK : DDM_ERR_HIP;
+        }
+    }
+    if (!G.cap && hipStreamCreateWithFlags(&G.cap, hipStreamNonBlocking) != hipSuccess) return DDM_ERR_HIP;
+    if (hipStreamBeginCapture(G.cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return DDM_ERR_HIP;
+    const int rc = enqueue(G.cap);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(G.cap, &graph);
+    if (rc != DDM_OK || ec != hipSuccess) {
+        if (graph) hipGraphDestroy(graph);
+        return rc != DDM_OK ? rc : DDM_ERR_HIP;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (ei != hipSuccess) return DDM_ERR_HIP;
+    if (G.lru.size() >= GraphCache::kMax) {
+        hipGraphExecDestroy(G.lru.back().second);
+        G.lru.pop_back();
+    }
+    G.lru.emplace_front(key, exec);
+    return hipGraphLaunch(exec, stream) == hipSuccess ? DDM_OK : DDM_ERR_HIP;
 }
 
 }  // namespace
@@ -464,6 +534,7 @@ int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, i
     if (!map_ok(Q, P.f) || !map_ok(R, P.f) || !out_idx || !out_score) return DDM_ERR_INVALID;
     if (!q_rows && NQ < M) return DDM_ERR_INVALID;
     if (!workspace || workspace_bytes < P.total) return DDM_ERR_WORKSPACE;
+    if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
     unsigned char *w = (unsigned char *)workspace;
     const void *q, *r;
     rc = maybe_repack(P.f, Q, NQ, w + P.o_rq, stream, &q);
@@ -502,8 +573,19 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
     if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
     if (capacity < P.k) return DDM_ERR_CAPACITY;
     if (!workspace || workspace_bytes < P.total) return DDM_ERR_WORKSPACE;
-    return frm_run(P, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts, workspace,
-                   stream);
+    if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DDM_ERR_HIP;
+    const GraphKey key = {(uint64_t)dev, (uint64_t)B, (uint64_t)(uintptr_t)D1, (uint64_t)H1, (uint64_t)W1,
+                          (uint64_t)(uintptr_t)D2, (uint64_t)H2, (uint64_t)W2, (uint64_t)d, (uint64_t)dtype,
+                          (uint64_t)grid_stride, (uint64_t)max_iter, (uint64_t)(uintptr_t)out_i,
+                          (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
+                          (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)seed_state,
+                          (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, 0, 0, 0, 0};
+    return run_graphed(key, stream, [&](hipStream_t s) {
+        return frm_run(P, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts, workspace,
+                       s);
+    });
 }
 
 int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
@@ -538,6 +620,7 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
     if ((nn12 == nullptr) != (s12 == nullptr)) return DDM_ERR_INVALID;
     if (capacity < std::min(P.N1, P.N2)) return DDM_ERR_CAPACITY;
     if (!workspace || workspace_bytes < P.total) return DDM_ERR_WORKSPACE;
+    if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
     unsigned char *w = (unsigned char *)workspace;
     const void *m1, *m2;
     rc = maybe_repack(P.f, D1, P.N1, w + P.o_r1, stream, &m1);

@@ -127,3 +127,33 @@ def test_determinism_full_size(ddm):
     r1 = ddm.mutual_nn(D1, D2); r2 = ddm.mutual_nn(D1, D2)
     for x, y in zip(r1, r2):
         assert torch.equal(x, y)
+
+
+def test_frm_graph_replays_match_direct_launches(ddm):
+    """FRM calls with unchanged arguments replay a cached HIP graph; every replay,
+    with unrelated work and host synchronisation in between, must equal a call made
+    with direct launches (sweep timing on forces those)."""
+    import torch
+    (p,) = synth.make_config("frm_512x384x24_f16")
+    D1, D2 = dev(p.D1, p.dtype), dev(p.D2, p.dtype)
+    buf = ddm.FrmBuffers(1, 512, 384, 512, 384, 24, torch.float16, 8, 10, D1.device)
+    ddm.profile_enable(2)
+    ddm.frm_match_into(D1, D2, 8, 10, buf)
+    torch.cuda.synchronize()
+    ddm.profile_read()
+    ddm.profile_enable(0)
+    ref = [t.clone() for t in (buf.out_i, buf.out_j, buf.out_s, buf.count, buf.state, buf.qcounts)]
+    for rep in range(4):
+        for t in (buf.out_i, buf.out_j, buf.state, buf.qcounts):
+            t.fill_(-7)
+        buf.out_s.fill_(float("nan")); buf.count.zero_()
+        x = torch.randn(1 << 20, device=D1.device).sum()      # unrelated work between replays
+        ddm.frm_match_into(D1, D2, 8, 10, buf)
+        torch.cuda.synchronize()
+        got = (buf.out_i, buf.out_j, buf.out_s, buf.count, buf.state, buf.qcounts)
+        n = int(ref[3][0])
+        assert int(buf.count[0]) == n, f"replay {rep}"
+        for a, b in zip(got, ref):
+            assert torch.equal(a[: max(n, 1)] if a.numel() == ref[0].numel() else a,
+                               b[: max(n, 1)] if b.numel() == ref[0].numel() else b), f"replay {rep}"
+        del x
