@@ -185,6 +185,28 @@ hipError_t launch_sweep_impl(const MapFmt &f, bool colmax, const SweepArgs &a, d
         else hipLaunchKernelGGL(KERNEL<DT_F32>, __VA_ARGS__);                                     \
     } while (0)
 
+// resolve kernels: dtype x queries per block
+#define DDM_QB_LAUNCH(DT, qb, KERNEL, ...)                                                        \
+    do {                                                                                          \
+        if ((qb) == 256) hipLaunchKernelGGL(HIP_KERNEL_NAME(KERNEL<DT, 256>), __VA_ARGS__);       \
+        else if ((qb) == 64) hipLaunchKernelGGL(HIP_KERNEL_NAME(KERNEL<DT, 64>), __VA_ARGS__);    \
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(KERNEL<DT, 16>), __VA_ARGS__);                    \
+    } while (0)
+#define DDM_DT_QB_SWITCH(dtype, qb, KERNEL, ...)                                                  \
+    do {                                                                                          \
+        if ((dtype) == DT_F16) DDM_QB_LAUNCH(DT_F16, qb, KERNEL, __VA_ARGS__);                    \
+        else if ((dtype) == DT_BF16) DDM_QB_LAUNCH(DT_BF16, qb, KERNEL, __VA_ARGS__);             \
+        else DDM_QB_LAUNCH(DT_F32, qb, KERNEL, __VA_ARGS__);                                      \
+    } while (0)
+
+// Queries per resolve block: large blocks amortise the phase-1 reduction, but
+// the launch should still give every CU several blocks.
+int resolve_qb(long long nq) {
+    for (int qb : {256, 64})
+        if (nq / qb >= 2048) return qb;
+    return 16;
+}
+
 #define DDM_CHECK(expr)                                                                           \
     do {                                                                                          \
         if ((expr) != hipSuccess) return DDM_ERR_HIP;                                             \
@@ -341,7 +363,7 @@ int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, in
     DDM_CHECK_LAUNCH();
 
     const long long b1 = (long long)P.N1 * f.ld * f.esz, b2 = (long long)P.N2 * f.ld * f.esz;
-    const int upd_blocks = (std::max(P.k, 1) * 16 + 255) / 256;
+    const int upd_blocks = (std::max(P.k, 1) + 15) / 16;
     if (P.k > 0) {
         for (int t = 0; t < P.max_iter; ++t) {
             for (int dir = 0; dir < 2; ++dir) {
@@ -456,15 +478,15 @@ int run_graphed(const GraphKey &key, hipStream_t stream, Enqueue enqueue) {
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(G.cap, &graph);
     if (rc != DDM_OK || ec != hipSuccess) {
-        if (graph) hipGraphDestroy(graph);
+        if (graph) (void)hipGraphDestroy(graph);
         return rc != DDM_OK ? rc : DDM_ERR_HIP;
     }
     hipGraphExec_t exec = nullptr;
     const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     if (ei != hipSuccess) return DDM_ERR_HIP;
     if (G.lru.size() >= GraphCache::kMax) {
-        hipGraphExecDestroy(G.lru.back().second);
+        (void)hipGraphExecDestroy(G.lru.back().second);
         G.lru.pop_back();
     }
     G.lru.emplace_front(key, exec);
@@ -550,8 +572,9 @@ int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, i
     ResolveArgs ra{};
     ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = M;
     ra.Q = a.Q; ra.qrows = q_rows; ra.nq = M; ra.R = a.R; ra.nref = N; ra.ld = P.f.ld; ra.d = d;
-    const int blocks = (M * 16 + 255) / 256;
-    DDM_DT_SWITCH(P.f.dtype, nn_resolve_kernel, dim3(blocks), dim3(256), 0, stream, ra, out_idx, out_score);
+    const int qb = resolve_qb(M);
+    DDM_DT_QB_SWITCH(P.f.dtype, qb, nn_resolve_kernel, dim3((M + qb - 1) / qb), dim3(256), 0, stream, ra, out_idx,
+                     out_score);
     DDM_CHECK_LAUNCH();
     return DDM_OK;
 }
@@ -643,8 +666,9 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
     ra.Q = a.Q; ra.nq = P.N1; ra.R = a.R; ra.nref = P.N2; ra.ld = P.f.ld; ra.d = d;
     int32_t *mj = (int32_t *)(w + P.o_mj);
     float *ms = (float *)(w + P.o_ms);
-    DDM_DT_SWITCH(P.f.dtype, mutual_rows_kernel, dim3((P.N1 * 16 + 255) / 256), dim3(256), 0, stream, ra,
-                  (const uint32_t *)cmax, mj, ms, nn12, s12);
+    const int qb = resolve_qb(P.N1);
+    DDM_DT_QB_SWITCH(P.f.dtype, qb, mutual_rows_kernel, dim3((P.N1 + qb - 1) / qb), dim3(256), 0, stream, ra,
+                     (const uint32_t *)cmax, mj, ms, nn12, s12);
     DDM_CHECK_LAUNCH();
     return compact_run(mj, ms, P.N1, P.N1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo), out_i, out_j,
                        out_score, capacity, out_count, stream);

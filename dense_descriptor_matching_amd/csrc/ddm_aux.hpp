@@ -30,34 +30,71 @@ __device__ __forceinline__ float dot_rows(const unsigned char *a, const unsigned
     return s;
 }
 
-// Called by all 16 lanes of a DPP row (sub = lane & 15) for one query x.
+// The 8 products of one 16-byte piece (fp16 or bf16), accumulated in element order.
 template <int DT>
-__device__ __forceinline__ void resolve_one(const uint64_t *part, int nchunks, long long rowcap, int x,
-                                            const unsigned char *qp, const unsigned char *R, int nref, int ld,
-                                            int d, int sub, int *j_out, float *s_out) {
+__device__ __forceinline__ float dot_piece(u32x4_t a, u32x4_t b, float s) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float a0, a1, b0, b1;
+        if constexpr (DT == DT_F16) {
+            a0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[w] & 0xffffu));
+            a1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[w] >> 16));
+            b0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[w] & 0xffffu));
+            b1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[w] >> 16));
+        } else {
+            a0 = __uint_as_float(a[w] << 16); a1 = __uint_as_float(a[w] & 0xffff0000u);
+            b0 = __uint_as_float(b[w] << 16); b1 = __uint_as_float(b[w] & 0xffff0000u);
+        }
+        s = fmaf(a0, b0, s);
+        s = fmaf(a1, b1, s);
+    }
+    return s;
+}
+
+// Rescan of one query's winning (group, slot): called by the 16 lanes of a row
+// (sub = lane & 15) with the query's merged partial key. Lane sub takes the
+// candidates t = sub, sub + 16, ... of the G; fp16/bf16 rows are read as whole
+// 16-byte pieces (rows hold ld = 8 * pieces elements, zero beyond d).
+template <int DT>
+__device__ __forceinline__ void rescan_one(uint64_t k, const unsigned char *qp, const unsigned char *R, int nref,
+                                           int ld, int d, int sub, int *j_out, float *s_out) {
     constexpr int ESZ = Tr<DT>::ESZ;
     constexpr int G = group_tiles(DT), GROUP = TILE * G;
-    uint64_t k = 0;
-    for (int ch = sub; ch < nchunks; ch += 16) {
-        const uint64_t v = part[(long long)ch * rowcap + x];
-        k = v > k ? v : k;
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        const uint64_t o = __shfl_xor(k, m, 16);
-        k = o > k ? o : k;
-    }
     const float mval = fkey_inv((uint32_t)(k >> 32));
     const uint32_t id = ~(uint32_t)k;
     const int j0 = (int)((id >> 4) * GROUP + (id & 15u) * G);
     float s = -INFINITY;
     int bj = 0x7fffffff;
+    if constexpr (DT == DT_F32) {
 #pragma unroll
-    for (int t = sub; t < G; t += 16) {          // ascending t: strict > keeps the lowest
-        const int j = j0 + t;
-        if (j < nref) {
-            const float v = dot_rows<DT>(qp, R + (long long)j * ld * ESZ, d);
-            if (v > s || bj == 0x7fffffff) { s = v; bj = j; }
+        for (int t = sub; t < G; t += 16) {      // ascending t: strict > keeps the lowest
+            const int j = j0 + t;
+            if (j < nref) {
+                const float v = dot_rows<DT>(qp, R + (long long)j * ld * ESZ, d);
+                if (v > s || bj == 0x7fffffff) { s = v; bj = j; }
+            }
+        }
+    } else {
+        constexpr int C = G / 16;
+        const u32x4_t *q4 = reinterpret_cast<const u32x4_t *>(qp);
+        const u32x4_t *r4[C];
+        float acc[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int j = j0 + sub + 16 * c;
+            r4[c] = reinterpret_cast<const u32x4_t *>(R + (long long)(j < nref ? j : nref - 1) * ld * ESZ);
+            acc[c] = 0.f;
+        }
+        const int np = ld / 8;
+        for (int p = 0; p < np; ++p) {
+            const u32x4_t qv = q4[p];
+#pragma unroll
+            for (int c = 0; c < C; ++c) acc[c] = dot_piece<DT>(qv, r4[c][p], acc[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {            // ascending t: strict > keeps the lowest
+            const int j = j0 + sub + 16 * c;
+            if (j < nref && (acc[c] > s || bj == 0x7fffffff)) { s = acc[c]; bj = j; }
         }
     }
 #pragma unroll
@@ -72,6 +109,59 @@ __device__ __forceinline__ void resolve_one(const uint64_t *part, int nchunks, l
     *s_out = mval;
 }
 
+// Resolution of QB consecutive queries per 256-thread block. Phase 1: TPQ =
+// 256 / QB threads per query take the maximum of its per-chunk partial keys,
+// consecutive threads on consecutive queries so that each chunk's slice is read
+// contiguously, then the TPQ partial maxima meet in LDS. Phase 2: sixteen lanes
+// per query rescan the winning group's candidates, 16 queries per round.
+// emit(valid, x, j, s, sub) is called by every lane in every round (wave-wide
+// ballots may follow). Blocks past nq return at once (nq may be device-side).
+template <int DT, int QB, class QPtr, class Emit>
+__device__ __forceinline__ void resolve_block(const uint64_t *part, int nchunks, long long rowcap, int nq,
+                                              const unsigned char *R, int nref, int ld, int d, QPtr qptr,
+                                              Emit emit) {
+    static_assert(QB % 16 == 0 && 256 % QB == 0, "QB divides the block");
+    constexpr int TPQ = 256 / QB;
+    __shared__ uint64_t red[256];
+    const int x0 = blockIdx.x * QB;
+    if (x0 >= nq) return;
+    {
+        const int q = (int)threadIdx.x % QB, slice = (int)threadIdx.x / QB;
+        const int x = x0 + q;
+        uint64_t k = 0;
+        if (x < nq) {
+#pragma unroll 8
+            for (int ch = slice; ch < nchunks; ch += TPQ) {
+                const uint64_t v = part[(long long)ch * rowcap + x];
+                k = v > k ? v : k;
+            }
+        }
+        red[threadIdx.x] = k;
+    }
+    __syncthreads();
+    if (TPQ > 1 && threadIdx.x < QB) {
+        uint64_t k = red[threadIdx.x];
+#pragma unroll
+        for (int t = 1; t < TPQ; ++t) {
+            const uint64_t v = red[t * QB + threadIdx.x];
+            k = v > k ? v : k;
+        }
+        red[threadIdx.x] = k;
+    }
+    if (TPQ > 1) __syncthreads();
+    const int sub = threadIdx.x & 15;
+#pragma unroll 1
+    for (int round = 0; round < QB / 16; ++round) {
+        const int r = round * 16 + (int)(threadIdx.x >> 4);
+        const int x = x0 + r;
+        const bool valid = x < nq;
+        int j = 0;
+        float s = 0.f;
+        if (valid) rescan_one<DT>(red[r], qptr(x), R, nref, ld, d, sub, &j, &s);
+        emit(valid, x, j, s, sub);
+    }
+}
+
 struct ResolveArgs {
     const uint64_t *rowpart; long long rowpart_bs; int nchunks; int rowcap;
     const unsigned char *Q; long long q_bs; const int32_t *qrows; long long qrows_bs;
@@ -80,15 +170,16 @@ struct ResolveArgs {
 };
 
 // Plain NN output: out_idx[x], out_score[x] for every query.
-template <int DT>
+template <int DT, int QB>
 __global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, int32_t *out_idx, float *out_score) {
-    const int x = (blockIdx.x * 256 + threadIdx.x) >> 4, sub = threadIdx.x & 15;
-    if (x >= a.nq) return;
-    const int qrow = a.qrows ? a.qrows[x] : x;
-    int j; float s;
-    resolve_one<DT>(a.rowpart, a.nchunks, a.rowcap, x, a.Q + (long long)qrow * a.ld * Tr<DT>::ESZ, a.R, a.nref,
-                    a.ld, a.d, sub, &j, &s);
-    if (sub == 0) { out_idx[x] = j; out_score[x] = s; }
+    resolve_block<DT, QB>(a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
+                      [&](int x) {
+                          const int qrow = a.qrows ? a.qrows[x] : x;
+                          return a.Q + (long long)qrow * a.ld * Tr<DT>::ESZ;
+                      },
+                      [&](bool valid, int x, int j, float s, int sub) {
+                          if (valid && sub == 0) { out_idx[x] = j; out_score[x] = s; }
+                      });
 }
 
 // ---------------------------------------------------------------------------
@@ -105,20 +196,19 @@ __global__ void __launch_bounds__(256) colmax_merge_kernel(const uint32_t *colpa
     colmax[j] = m;
 }
 
-template <int DT>
+template <int DT, int QB>
 __global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint32_t *colmax, int32_t *match_j,
                                                           float *match_s, int32_t *nn12, float *s12) {
-    const int x = (blockIdx.x * 256 + threadIdx.x) >> 4, sub = threadIdx.x & 15;
-    if (x >= a.nq) return;
-    int j; float s;
-    resolve_one<DT>(a.rowpart, a.nchunks, a.rowcap, x, a.Q + (long long)x * a.ld * Tr<DT>::ESZ, a.R, a.nref,
-                    a.ld, a.d, sub, &j, &s);
-    if (sub == 0) {
-        const bool mutual = colmax[j] == fkey(s);
-        match_j[x] = mutual ? j : -1;
-        match_s[x] = s;
-        if (nn12) { nn12[x] = j; s12[x] = s; }
-    }
+    resolve_block<DT, QB>(a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
+                      [&](int x) { return a.Q + (long long)x * a.ld * Tr<DT>::ESZ; },
+                      [&](bool valid, int x, int j, float s, int sub) {
+                          if (valid && sub == 0) {
+                              const bool mutual = colmax[j] == fkey(s);
+                              match_j[x] = mutual ? j : -1;
+                              match_s[x] = s;
+                              if (nn12) { nn12[x] = j; s12[x] = s; }
+                          }
+                      });
 }
 
 // ---------------------------------------------------------------------------
@@ -156,51 +246,48 @@ __global__ void __launch_bounds__(256) frm_init_kernel(FrmState st, int k, int k
 
 // One half-step's update: resolve each active query, apply the cycle test and
 // append the seeds that stay active to the next list (wave ballot + one atomic
-// per wave; list order does not affect any result).
+// per wave; list order does not affect any result). 16 queries per block.
 template <int DT>
 __global__ void __launch_bounds__(256) frm_update_kernel(ResolveArgs a, FrmState st, int h, int backward,
                                                          int iter) {
     const int pair = blockIdx.y;
     const int cur = h & 1, nxt = cur ^ 1;
     const long long ko = pair * st.k_bs;
-    const int32_t *counts = st.counts + pair * st.cnt_bs;
+    int32_t *counts = st.counts + pair * st.cnt_bs;
     const int nq = counts[h];
-    const int x = (blockIdx.x * 256 + threadIdx.x) >> 4, sub = threadIdx.x & 15;
     const int lane = threadIdx.x & 63;
-    bool keep = false;
-    int seed = 0, j = 0;
-    if (x < nq) {
-        seed = st.act[cur][ko + x];
-        const int qrow = st.qrows[cur][ko + x];
-        float s;
-        resolve_one<DT>(a.rowpart + pair * a.rowpart_bs, a.nchunks, a.rowcap, x,
-                        a.Q + pair * a.q_bs + (long long)qrow * a.ld * Tr<DT>::ESZ, a.R + pair * a.r_bs, a.nref,
-                        a.ld, a.d, sub, &j, &s);
-        if (sub == 0) {
-            if (!backward) {
-                keep = (j != st.v[ko + seed]);
-                st.v[ko + seed] = j;
-                st.score[ko + seed] = s;
-            } else {
-                keep = (j != st.u[ko + seed]);
-                st.u[ko + seed] = j;
+    const unsigned char *Q = a.Q + pair * a.q_bs;
+    resolve_block<DT, 16>(
+        a.rowpart + pair * a.rowpart_bs, a.nchunks, a.rowcap, nq, a.R + pair * a.r_bs, a.nref, a.ld, a.d,
+        [&](int x) { return Q + (long long)st.qrows[cur][ko + x] * a.ld * Tr<DT>::ESZ; },
+        [&](bool valid, int x, int j, float s, int sub) {
+            bool keep = false;
+            int seed = 0;
+            if (valid && sub == 0) {
+                seed = st.act[cur][ko + x];
+                if (!backward) {
+                    keep = (j != st.v[ko + seed]);
+                    st.v[ko + seed] = j;
+                    st.score[ko + seed] = s;
+                } else {
+                    keep = (j != st.u[ko + seed]);
+                    st.u[ko + seed] = j;
+                }
+                if (!keep) st.conv[ko + seed] = iter;
             }
-            if (!keep) st.conv[ko + seed] = iter;
-        }
-    }
-    // stream compaction of the seeds that stay active
-    const uint64_t ball = __ballot(keep);
-    const int n = __popcll(ball);
-    int base = 0;
-    if (n > 0) {
-        if (lane == 0) base = atomicAdd(st.counts + pair * st.cnt_bs + h + 1, n);
-        base = __shfl(base, 0);
-        if (keep) {
-            const int pos = base + __popcll(ball & ((1ull << lane) - 1ull));
-            st.act[nxt][ko + pos] = seed;
-            st.qrows[nxt][ko + pos] = j;
-        }
-    }
+            const uint64_t ball = __ballot(keep);
+            const int n = __popcll(ball);
+            if (n > 0) {
+                int base = 0;
+                if (lane == 0) base = atomicAdd(counts + h + 1, n);
+                base = __shfl(base, 0);
+                if (keep) {
+                    const int pos = base + __popcll(ball & ((1ull << lane) - 1ull));
+                    st.act[nxt][ko + pos] = seed;
+                    st.qrows[nxt][ko + pos] = j;
+                }
+            }
+        });
 }
 
 // Converged seeds -> dense match array indexed by image-1 pixel (every seed
