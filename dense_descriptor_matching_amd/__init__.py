@@ -53,6 +53,8 @@ def _declare(lib):
     lib.ddm_mutual_workspace_bytes.argtypes = [I, I, I, I, I, I]; lib.ddm_mutual_workspace_bytes.restype = SZ
     lib.ddm_mutual_nn.argtypes = [P, I, I, P, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
     lib.ddm_mutual_nn.restype = I
+    lib.ddm_frm_set_mode.argtypes = [I]; lib.ddm_frm_set_mode.restype = I
+    lib.ddm_frm_get_mode.argtypes = []; lib.ddm_frm_get_mode.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
     lib.ddm_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]; lib.ddm_profile_read.restype = I
     return lib
@@ -104,8 +106,22 @@ def to_xy(idx: torch.Tensor, W: int):
     return idx % W, torch.div(idx, W, rounding_mode="floor")
 
 
+FRM_PER_HALF_STEP = 0      # one sweep + one update launch per half-step (default)
+FRM_LOOP = 1               # every iteration in one cooperative loop kernel
+
+
+def frm_set_mode(mode: int):
+    """Select how FRM calls execute (process-wide; results are identical)."""
+    _rc(lib().ddm_frm_set_mode(mode), "ddm_frm_set_mode")
+
+
+def frm_get_mode() -> int:
+    return lib().ddm_frm_get_mode()
+
+
 def profile_enable(mask: int):
-    """Bracket later sweep launches with HIP events (bit 0: mutual sweep, bit 1: NN/FRM sweeps)."""
+    """Bracket later sweep launches with HIP events (bit 0: mutual sweep, bit 1: NN and FRM
+    sweeps and the FRM loop kernel as a whole)."""
     _rc(lib().ddm_profile_enable(mask), "ddm_profile_enable")
 
 
@@ -141,6 +157,13 @@ def nn(Q: torch.Tensor, R: torch.Tensor, q_rows: torch.Tensor | None = None):
 
 
 # ------------------------------------------------------------------- FRM
+def _count(n) -> int:
+    n = int(n)
+    if n < 0:
+        raise DDMError(-5, "FRM loop-kernel grid synchronisation failed (out_count = -1)")
+    return n
+
+
 class FrmBuffers:
     """Preallocated outputs + workspace for repeated FRM calls on one shape."""
 
@@ -197,7 +220,7 @@ def frm_match(D1: torch.Tensor, D2: torch.Tensor, grid_stride: int = 8, max_iter
     H2, W2, _ = D2.shape
     buf = FrmBuffers(1, H1, W1, H2, W2, d, D1.dtype, grid_stride, max_iter, D1.device, with_state=return_state)
     frm_match_into(D1, D2, grid_stride, max_iter, buf)
-    n = int(buf.count[0].item())
+    n = _count(buf.count[0].item())
     res = (buf.out_i[:n].clone(), buf.out_j[:n].clone(), buf.out_s[:n].clone())
     if not return_state:
         return res
@@ -216,7 +239,7 @@ def frm_match_batched(D1: torch.Tensor, D2: torch.Tensor, grid_stride: int = 8, 
     out = []
     for b in range(B):
         o = b * buf.cap
-        n = counts[b]
+        n = _count(counts[b])
         item = (buf.out_i[o:o + n].clone(), buf.out_j[o:o + n].clone(), buf.out_s[o:o + n].clone())
         if return_state:
             st = buf.state.view(B, buf.cap, 4)[b, :buf.k, :3].clone()
@@ -269,4 +292,5 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False):
 
 
 __all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "mutual_nn", "mutual_nn_into", "seed_count",
-           "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH", "profile_enable", "profile_read"]
+           "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH", "profile_enable", "profile_read",
+           "frm_set_mode", "frm_get_mode", "FRM_PER_HALF_STEP", "FRM_LOOP"]

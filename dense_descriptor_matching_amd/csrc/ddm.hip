@@ -3,12 +3,13 @@
 // Every step of every call runs in the kernels of ddm_sweep.hpp / ddm_aux.hpp;
 // the host only checks arguments and enqueues.
 #include "../../include/ddm.h"
-#include "ddm_aux.hpp"
+#include "ddm_frm.hpp"
 
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <array>
+#include <atomic>
 #include <list>
 #include <mutex>
 #include <vector>
@@ -27,6 +28,7 @@ constexpr int nw_for(int dt) { return dt == DT_F32 ? 4 : 8; }
 constexpr int rq_for(int dt, int nkb) { return dt == DT_F32 ? 2 : (nkb <= 2 ? 6 : 4); }
 constexpr size_t LDS_MAX = 160 * 1024;
 constexpr long long MIN_WG = 256;          // one workgroup per CU
+constexpr size_t LOOP_LDS_MAX = LDS_MAX - 1024;   // the FRM loop kernel keeps a few LDS words of its own
 constexpr int MAX_PIX = 1 << 27;
 
 struct MapFmt {
@@ -64,10 +66,10 @@ struct Bump {
     size_t take(size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; }
 };
 
-int chunk_limit(const MapFmt &f, bool colmax) {
+int chunk_limit(const MapFmt &f, bool colmax, size_t lds_max = LDS_MAX) {
     const size_t per_ref = (size_t)f.tile_bytes() / TILE + (colmax ? 4 : 0);
     const int grp = f.group();
-    int c = (int)(LDS_MAX / per_ref) / grp * grp;
+    int c = (int)(lds_max / per_ref) / grp * grp;
     return std::max(c, grp);
 }
 
@@ -121,6 +123,79 @@ hipError_t sweep_switch(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 g
     }
 }
 
+// Format dispatch for the loop kernel: fn(dtype, pieces, K blocks) as constants.
+template <int DT, class Fn>
+hipError_t np_dispatch(const MapFmt &f, Fn &&fn) {
+    using std::integral_constant;
+    using D = integral_constant<int, DT>;
+    if constexpr (DT == DT_F32) {
+        if (f.nkb == 8) return fn(D{}, integral_constant<int, 0>{}, integral_constant<int, 8>{});
+        return fn(D{}, integral_constant<int, 0>{}, integral_constant<int, 32>{});
+    } else {
+        switch (f.np) {
+        case 1: return fn(D{}, integral_constant<int, 1>{}, integral_constant<int, 1>{});
+        case 2: return fn(D{}, integral_constant<int, 2>{}, integral_constant<int, 1>{});
+        case 3: return fn(D{}, integral_constant<int, 3>{}, integral_constant<int, 1>{});
+        case 4: return fn(D{}, integral_constant<int, 4>{}, integral_constant<int, 1>{});
+        case 6: return fn(D{}, integral_constant<int, 6>{}, integral_constant<int, 2>{});
+        case 8: return fn(D{}, integral_constant<int, 8>{}, integral_constant<int, 2>{});
+        case 12: return fn(D{}, integral_constant<int, 12>{}, integral_constant<int, 3>{});
+        case 16: return fn(D{}, integral_constant<int, 16>{}, integral_constant<int, 4>{});
+        default: return hipErrorInvalidValue;
+        }
+    }
+}
+template <class Fn>
+hipError_t fmt_dispatch(const MapFmt &f, Fn &&fn) {
+    switch (f.dtype) {
+    case DT_F16: return np_dispatch<DT_F16>(f, fn);
+    case DT_BF16: return np_dispatch<DT_BF16>(f, fn);
+    default: return np_dispatch<DT_F32>(f, fn);
+    }
+}
+
+// FRM phase kernels of one map format. which = 0: per-half-step sweep of
+// half-step h (plain launch), 1: loop kernel from half-step h (cooperative
+// launch). The grid is min(ntask, workgroups the device keeps resident).
+// launch == false only raises the kernels' dynamic-LDS limit.
+template <int DT, int NP, int NKB>
+hipError_t launch_frm_t(int which, const FrmArgs *a, int h, size_t lds, long long ntask, hipStream_t s,
+                        bool launch) {
+    constexpr int rq = rq_for(DT, NKB);
+    constexpr int nw = nw_for(DT);
+    auto ks = frm_sweep_kernel<DT, NP, NKB, rq, nw>;
+    auto kl = frm_loop_kernel<DT, NP, NKB, rq, nw>;
+    if (!launch) {
+        hipError_t e = hipFuncSetAttribute((const void *)ks, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)LOOP_LDS_MAX);
+        if (e != hipSuccess) return e;
+        return hipFuncSetAttribute((const void *)kl, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LOOP_LDS_MAX);
+    }
+    int dev = 0, ncu = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, which == 0 ? (const void *)ks : (const void *)kl,
+                                                         nw * 64, lds);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1 || ncu < 1) return hipErrorInvalidConfiguration;
+    const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(ntask, (long long)per_cu * ncu));
+    if (which == 0) {
+        hipLaunchKernelGGL(ks, dim3(grid), dim3(nw * 64), lds, s, *a, h);
+        return hipGetLastError();
+    }
+    void *args[] = {(void *)a, (void *)&h};
+    return hipLaunchCooperativeKernel((const void *)kl, dim3(grid), dim3(nw * 64), args, (unsigned)lds, s);
+}
+
+hipError_t frm_switch(const MapFmt &f, int which, const FrmArgs *a, int h, size_t lds, long long ntask,
+                      hipStream_t s, bool launch) {
+    return fmt_dispatch(f, [&](auto dt, auto np, auto nkb) {
+        return launch_frm_t<decltype(dt)::value, decltype(np)::value, decltype(nkb)::value>(which, a, h, lds, ntask,
+                                                                                          s, launch);
+    });
+}
+
 // Raise the dynamic-LDS limit of every sweep instantiation once per process.
 hipError_t prepare_kernels() {
     static std::once_flag once;
@@ -135,6 +210,10 @@ hipError_t prepare_kernels() {
                     SweepArgs a{};
                     hipError_t e = sweep_switch(f, cm != 0, a, dim3(1), 0, nullptr, false);
                     if (e != hipSuccess) status = e;
+                    if (cm == 0) {
+                        e = frm_switch(f, 0, nullptr, 0, 0, 0, nullptr, false);
+                        if (e != hipSuccess) status = e;
+                    }
                 }
     });
     return status;
@@ -150,12 +229,11 @@ struct Profiler {
 };
 Profiler &prof() { static Profiler p; return p; }
 
-hipError_t launch_sweep_impl(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s);
-
-hipError_t launch_sweep(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s) {
+// Enqueue fn(), bracketed by two events on s when timing of `kind` is on.
+template <class Fn>
+hipError_t with_events(int kind, hipStream_t s, Fn fn) {
     Profiler &P = prof();
-    const int kind = colmax ? 1 : 2;
-    if (!(P.mask & kind)) return launch_sweep_impl(f, colmax, a, grid, s);
+    if (!(P.mask & kind)) return fn();
     std::pair<hipEvent_t, hipEvent_t> ev;
     {
         std::lock_guard<std::mutex> g(P.mu);
@@ -167,11 +245,17 @@ hipError_t launch_sweep(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 g
         }
     }
     hipError_t e = hipEventRecord(ev.first, s);
-    if (e == hipSuccess) e = launch_sweep_impl(f, colmax, a, grid, s);
+    if (e == hipSuccess) e = fn();
     if (e == hipSuccess) e = hipEventRecord(ev.second, s);
     std::lock_guard<std::mutex> g(P.mu);
     P.pending.push_back(ev);
     return e;
+}
+
+hipError_t launch_sweep_impl(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s);
+
+hipError_t launch_sweep(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s) {
+    return with_events(colmax ? 1 : 2, s, [&] { return launch_sweep_impl(f, colmax, a, grid, s); });
 }
 
 hipError_t launch_sweep_impl(const MapFmt &f, bool colmax, const SweepArgs &a, dim3 grid, hipStream_t s) {
@@ -278,11 +362,12 @@ struct FrmPlan {
     int chunk1, chunk2, nch1, nch2, qblocks, nblk;
     long long k_bs, cnt_bs, part_bs;
     size_t o_u, o_v, o_conv, o_score, o_act0, o_act1, o_qr0, o_qr1, o_counts, o_part, o_mj, o_ms, o_bc, o_bo,
-        o_r1, o_r2, total;
+        o_r1, o_r2, o_ctl, total;
+    size_t loop_lds;       // dynamic LDS of the loop kernel
 };
 
 int frm_chunk(const MapFmt &f, int nref, long long wg_other) {
-    int chunk = chunk_limit(f, false);
+    int chunk = chunk_limit(f, false, LOOP_LDS_MAX);
     while (chunk > f.group() && wg_other * ((nref + chunk - 1) / chunk) < MIN_WG) chunk -= f.group();
     return chunk;
 }
@@ -306,7 +391,8 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
     p->nblk = (p->N1 + CB - 1) / CB;
     p->k_bs = kk;
     p->cnt_bs = (long long)align_up((size_t)p->nhalf + 1, 64);
-    p->part_bs = (long long)std::max(p->nch1, p->nch2) * kk;
+    // partial slots of the runtime split: chunks x sub-chunks x rows per slot <= chunks x all query blocks
+    p->part_bs = (long long)std::max(p->nch1, p->nch2) * p->qblocks * sbr;
     Bump b;
     const size_t kb = (size_t)B * kk * 4;
     p->o_u = b.take(kb); p->o_v = b.take(kb); p->o_conv = b.take(kb); p->o_score = b.take(kb);
@@ -319,16 +405,20 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
     p->o_bo = b.take((size_t)B * p->nblk * 4);
     p->o_r1 = p->f.repack ? b.take((size_t)B * p->N1 * p->f.ld * 2) : 0;
     p->o_r2 = p->f.repack ? b.take((size_t)B * p->N2 * p->f.ld * 2) : 0;
+    p->o_ctl = b.take(256);
     p->total = b.off;
+    p->loop_lds = std::max(sweep_lds(p->f, std::max(p->chunk1, p->chunk2), false),
+                           (size_t)nw_for(dtype) * 64 * sizeof(uint64_t));
     return DDM_OK;
 }
 
 int compact_run(const int32_t *mj, const float *ms, long long n_bs, int n, int B, int nblk, int32_t *bc, int32_t *bo,
-                int32_t *out_i, int32_t *out_j, float *out_s, long long out_bs, int32_t *out_count, hipStream_t s) {
+                int32_t *out_i, int32_t *out_j, float *out_s, long long out_bs, int32_t *out_count, hipStream_t s,
+                const int32_t *err = nullptr) {
     hipLaunchKernelGGL(compact_count_kernel, dim3(nblk, B), dim3(256), 0, s, mj, n_bs, n, bc, nblk);
     DDM_CHECK_LAUNCH();
     hipLaunchKernelGGL(compact_scan_kernel, dim3(B), dim3(256), 0, s, (const int32_t *)bc, bo, nblk, out_count,
-                       (int)out_bs);
+                       (int)out_bs, err);
     DDM_CHECK_LAUNCH();
     hipLaunchKernelGGL(compact_scatter_kernel, dim3(nblk, B), dim3(256), 0, s, mj, ms, n_bs, n,
                        (const int32_t *)bo, nblk, out_i, out_j, out_s, out_bs, (int)out_bs);
@@ -336,9 +426,41 @@ int compact_run(const int32_t *mj, const float *ms, long long n_bs, int n, int B
     return DDM_OK;
 }
 
+// Sweep and resolve arguments of one FRM direction (0: image 1 -> 2, 1: back).
+void frm_dir_args(const FrmPlan &P, const void *m1, const void *m2, uint64_t *part, int dir, SweepArgs *a,
+                  ResolveArgs *r) {
+    const MapFmt &f = P.f;
+    const long long b1 = (long long)P.N1 * f.ld * f.esz, b2 = (long long)P.N2 * f.ld * f.esz;
+    *a = SweepArgs{};
+    a->Q = (const unsigned char *)(dir == 0 ? m1 : m2);
+    a->R = (const unsigned char *)(dir == 0 ? m2 : m1);
+    a->q_bs = dir == 0 ? b1 : b2;
+    a->r_bs = dir == 0 ? b2 : b1;
+    a->qrows_bs = P.k_bs;
+    a->qcount_bs = P.cnt_bs;
+    a->rowpart = part; a->rowpart_bs = P.part_bs;
+    a->nq = P.k;
+    a->nref = dir == 0 ? P.N2 : P.N1;
+    a->ld = f.ld;
+    a->chunk = dir == 0 ? P.chunk2 : P.chunk1;
+    a->nchunks = dir == 0 ? P.nch2 : P.nch1;
+    a->sb_per_wg = 1;
+    a->rowcap = (int)P.k_bs;
+    const int split = (int)std::max<long long>(1, MIN_WG / P.B);      // fill the device across the batch
+    a->split = split; a->qblocks = P.qblocks; a->split_rows = f.sb_rows();
+    *r = ResolveArgs{};
+    r->rowpart = part; r->rowpart_bs = P.part_bs; r->nchunks = a->nchunks; r->rowcap = (int)P.k_bs;
+    r->Q = a->Q; r->q_bs = a->q_bs; r->nq = P.k;
+    r->R = a->R; r->r_bs = a->r_bs; r->nref = a->nref; r->ld = f.ld; r->d = f.d;
+    r->split = split; r->qblocks = P.qblocks; r->split_rows = f.sb_rows(); r->chunk_groups = a->chunk / f.group();
+}
+
+// Half-steps [0, h_loop) run as one sweep and one update launch each, the
+// rest (all of them in the loop mode) in one cooperative loop kernel that
+// stops when no seed is active. The whole sequence can be captured into a graph.
 int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, int32_t *out_j, float *out_score,
             int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *ws,
-            hipStream_t s) {
+            hipStream_t s, int h_loop) {
     unsigned char *w = (unsigned char *)ws;
     const MapFmt &f = P.f;
     const void *m1, *m2;
@@ -356,45 +478,32 @@ int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, in
     st.match_j = (int32_t *)(w + P.o_mj); st.match_s = (float *)(w + P.o_ms);
     st.k_bs = P.k_bs; st.cnt_bs = P.cnt_bs; st.n1_bs = P.N1;
     uint64_t *part = (uint64_t *)(w + P.o_part);
+    uint32_t *ctl = (uint32_t *)(w + P.o_ctl);
 
     const int init_blocks = (int)std::min<long long>((std::max(P.k, P.N1) + 255) / 256, 4096);
     hipLaunchKernelGGL(frm_init_kernel, dim3(init_blocks, P.B), dim3(256), 0, s, st, P.k, std::max(P.kx, 1),
-                       P.W1, P.S, P.N1, P.nhalf);
+                       P.W1, P.S, P.N1, P.nhalf, ctl);
     DDM_CHECK_LAUNCH();
 
-    const long long b1 = (long long)P.N1 * f.ld * f.esz, b2 = (long long)P.N2 * f.ld * f.esz;
-    const int upd_blocks = (std::max(P.k, 1) + 15) / 16;
     if (P.k > 0) {
-        for (int t = 0; t < P.max_iter; ++t) {
-            for (int dir = 0; dir < 2; ++dir) {
-                const int h = 2 * t + dir;
-                SweepArgs a{};
-                a.Q = (const unsigned char *)(dir == 0 ? m1 : m2);
-                a.R = (const unsigned char *)(dir == 0 ? m2 : m1);
-                a.q_bs = dir == 0 ? b1 : b2;
-                a.r_bs = dir == 0 ? b2 : b1;
-                a.qrows = st.qrows[h & 1]; a.qrows_bs = P.k_bs;
-                a.qcount = st.counts + h; a.qcount_bs = P.cnt_bs;
-                a.rowpart = part; a.rowpart_bs = P.part_bs;
-                a.colpart = nullptr; a.colpart_bs = 0;
-                a.nq = P.k;
-                a.nref = dir == 0 ? P.N2 : P.N1;
-                a.ld = f.ld;
-                a.chunk = dir == 0 ? P.chunk2 : P.chunk1;
-                a.nchunks = dir == 0 ? P.nch2 : P.nch1;
-                a.sb_per_wg = 1;
-                a.rowcap = (int)P.k_bs;
-                DDM_CHECK(launch_sweep(f, false, a, dim3(a.nchunks, P.qblocks, P.B), s));
-
-                ResolveArgs r{};
-                r.rowpart = part; r.rowpart_bs = P.part_bs; r.nchunks = a.nchunks; r.rowcap = (int)P.k_bs;
-                r.Q = a.Q; r.q_bs = a.q_bs; r.qrows = nullptr; r.qrows_bs = 0;
-                r.qcount = nullptr; r.qcount_bs = 0; r.nq = P.k;
-                r.R = a.R; r.r_bs = a.r_bs; r.nref = a.nref; r.ld = f.ld; r.d = f.d;
-                DDM_DT_SWITCH(f.dtype, frm_update_kernel, dim3(upd_blocks, P.B), dim3(256), 0, s, r, st, h, dir,
-                              t + 1);
-                DDM_CHECK_LAUNCH();
-            }
+        FrmArgs fa{};
+        frm_dir_args(P, m1, m2, part, 0, &fa.sw[0], &fa.rs[0]);
+        frm_dir_args(P, m1, m2, part, 1, &fa.sw[1], &fa.rs[1]);
+        fa.st = st; fa.B = P.B; fa.nhalf = P.nhalf; fa.k = P.k; fa.qblocks = P.qblocks;
+        fa.nch[0] = P.nch2; fa.nch[1] = P.nch1;
+        fa.bar = ctl; fa.err = (int32_t *)(ctl + 32);
+        const long long sweep_tasks = (long long)P.B * P.qblocks * std::max(P.nch1, P.nch2);
+        const long long upd_tasks = (long long)P.B * ((P.k + 15) / 16);
+        for (int h = 0; h < std::min(h_loop, P.nhalf); ++h) {
+            DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, 0, &fa, h, P.loop_lds, sweep_tasks, s, true); }));
+            DDM_DT_SWITCH(f.dtype, frm_update_kernel, dim3((unsigned)std::min<long long>(upd_tasks, 2048)),
+                          dim3(256), 0, s, fa, h);
+            DDM_CHECK_LAUNCH();
+        }
+        if (h_loop < P.nhalf) {
+            const int qb = nw_for(f.dtype) * 64 / 16;
+            const long long ntask = std::max(sweep_tasks, (long long)P.B * ((P.k + qb - 1) / qb));
+            DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, 1, &fa, h_loop, P.loop_lds, ntask, s, true); }));
         }
     }
     const int col_blocks = (int)std::min<long long>((std::max(P.k, 1) + 255) / 256, 4096);
@@ -402,7 +511,8 @@ int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, in
                        (const int32_t *)st.counts, query_counts, P.nhalf);
     DDM_CHECK_LAUNCH();
     return compact_run(st.match_j, st.match_s, P.N1, P.N1, P.B, P.nblk, (int32_t *)(w + P.o_bc),
-                       (int32_t *)(w + P.o_bo), out_i, out_j, out_score, capacity, out_count, s);
+                       (int32_t *)(w + P.o_bo), out_i, out_j, out_score, capacity, out_count, s,
+                       (const int32_t *)(ctl + 32));
 }
 
 // -------------------------------------------------------------- mutual plan
@@ -441,6 +551,21 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p)
     p->o_r2 = p->f.repack ? b.take((size_t)p->N2 * p->f.ld * 2) : 0;
     p->total = b.off;
     return DDM_OK;
+}
+
+// ------------------------------------------------------------- FRM mode
+std::atomic<int> &frm_mode() { static std::atomic<int> m{DDM_FRM_PER_HALF_STEP}; return m; }
+
+bool cooperative_ok(int dev) {
+    static std::mutex mu;
+    static std::vector<int> known;      // per device: 0 unknown, 1 yes, 2 no
+    std::lock_guard<std::mutex> g(mu);
+    if ((int)known.size() <= dev) known.resize(dev + 1, 0);
+    if (known[dev] == 0) {
+        int v = 0;
+        known[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && v) ? 1 : 2;
+    }
+    return known[dev] == 1;
 }
 
 // ---------------------------------------------------------- graph replay
@@ -496,7 +621,6 @@ int run_graphed(const GraphKey &key, hipStream_t stream, Enqueue enqueue) {
 }  // namespace
 
 // ===================================================================== C ABI
-// ===================================================================== C ABI
 extern "C" {
 
 const char *ddm_status_str(int status) {
@@ -512,6 +636,14 @@ const char *ddm_status_str(int status) {
 }
 
 int64_t ddm_seed_count(int H, int W, int grid_stride) { return seed_count(H, W, grid_stride); }
+
+int ddm_frm_set_mode(int mode) {
+    if (mode != DDM_FRM_PER_HALF_STEP && mode != DDM_FRM_LOOP) return DDM_ERR_INVALID;
+    frm_mode().store(mode);
+    return DDM_OK;
+}
+
+int ddm_frm_get_mode(void) { return frm_mode().load(); }
 
 int ddm_profile_enable(int mask) {
     if (mask < 0 || mask > 3) return DDM_ERR_INVALID;
@@ -599,15 +731,17 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
     if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DDM_ERR_HIP;
-    const GraphKey key = {(uint64_t)dev, (uint64_t)B, (uint64_t)(uintptr_t)D1, (uint64_t)H1, (uint64_t)W1,
+    GraphKey key = {(uint64_t)dev, (uint64_t)B, (uint64_t)(uintptr_t)D1, (uint64_t)H1, (uint64_t)W1,
                           (uint64_t)(uintptr_t)D2, (uint64_t)H2, (uint64_t)W2, (uint64_t)d, (uint64_t)dtype,
                           (uint64_t)grid_stride, (uint64_t)max_iter, (uint64_t)(uintptr_t)out_i,
                           (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)seed_state,
                           (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, 0, 0, 0, 0};
+    const int h_loop = (frm_mode() == DDM_FRM_LOOP && cooperative_ok(dev)) ? 0 : P.nhalf;
+    key[20] = (uint64_t)h_loop;
     return run_graphed(key, stream, [&](hipStream_t s) {
         return frm_run(P, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts, workspace,
-                       s);
+                       s, h_loop);
     });
 }
 

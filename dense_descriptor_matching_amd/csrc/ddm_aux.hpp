@@ -109,21 +109,22 @@ __device__ __forceinline__ void rescan_one(uint64_t k, const unsigned char *qp, 
     *s_out = mval;
 }
 
-// Resolution of QB consecutive queries per 256-thread block. Phase 1: TPQ =
-// 256 / QB threads per query take the maximum of its per-chunk partial keys,
-// consecutive threads on consecutive queries so that each chunk's slice is read
-// contiguously, then the TPQ partial maxima meet in LDS. Phase 2: sixteen lanes
-// per query rescan the winning group's candidates, 16 queries per round.
-// emit(valid, x, j, s, sub) is called by every lane in every round (wave-wide
-// ballots may follow). Blocks past nq return at once (nq may be device-side).
-template <int DT, int QB, class QPtr, class Emit>
-__device__ __forceinline__ void resolve_block(const uint64_t *part, int nchunks, long long rowcap, int nq,
-                                              const unsigned char *R, int nref, int ld, int d, QPtr qptr,
-                                              Emit emit) {
-    static_assert(QB % 16 == 0 && 256 % QB == 0, "QB divides the block");
-    constexpr int TPQ = 256 / QB;
-    __shared__ uint64_t red[256];
-    const int x0 = blockIdx.x * QB;
+// Resolution of query block blk (QB consecutive queries) by an NT-thread
+// workgroup. Phase 1: TPQ = NT / QB threads per query take the maximum of its
+// per-chunk partial keys, consecutive threads on consecutive queries so that
+// each chunk's slice is read contiguously; the TPQ maxima meet in red[NT] (LDS).
+// Phase 2: sixteen lanes per query rescan the winning group's candidates,
+// NT / 16 queries per round. emit(valid, x, j, s, sub) is called by every lane
+// in every round (wave-wide ballots may follow). A block past nq returns at
+// once (nq may come from device memory; the test is uniform over the block).
+// The caller separates two uses of red by a barrier.
+template <int DT, int QB, int NT, class QPtr, class Emit>
+__device__ __forceinline__ void resolve_block(int blk, uint64_t *red, const uint64_t *part, int nchunks,
+                                              long long rowcap, int nq, const unsigned char *R, int nref, int ld,
+                                              int d, QPtr qptr, Emit emit) {
+    static_assert(QB % 16 == 0 && NT % QB == 0 && QB % (NT / 16) == 0, "QB and NT");
+    constexpr int TPQ = NT / QB, PER_ROUND = NT / 16;
+    const int x0 = blk * QB;
     if (x0 >= nq) return;
     {
         const int q = (int)threadIdx.x % QB, slice = (int)threadIdx.x / QB;
@@ -151,8 +152,8 @@ __device__ __forceinline__ void resolve_block(const uint64_t *part, int nchunks,
     if (TPQ > 1) __syncthreads();
     const int sub = threadIdx.x & 15;
 #pragma unroll 1
-    for (int round = 0; round < QB / 16; ++round) {
-        const int r = round * 16 + (int)(threadIdx.x >> 4);
+    for (int round = 0; round < QB / PER_ROUND; ++round) {
+        const int r = round * PER_ROUND + (int)(threadIdx.x >> 4);
         const int x = x0 + r;
         const bool valid = x < nq;
         int j = 0;
@@ -167,12 +168,14 @@ struct ResolveArgs {
     const unsigned char *Q; long long q_bs; const int32_t *qrows; long long qrows_bs;
     const int32_t *qcount; long long qcount_bs; int nq;
     const unsigned char *R; long long r_bs; int nref; int ld; int d;
+    int split, qblocks, split_rows, chunk_groups;   // runtime split of the sweep (SweepArgs)
 };
 
 // Plain NN output: out_idx[x], out_score[x] for every query.
 template <int DT, int QB>
 __global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, int32_t *out_idx, float *out_score) {
-    resolve_block<DT, QB>(a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
+    __shared__ uint64_t red[256];
+    resolve_block<DT, QB, 256>(blockIdx.x, red, a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
                       [&](int x) {
                           const int qrow = a.qrows ? a.qrows[x] : x;
                           return a.Q + (long long)qrow * a.ld * Tr<DT>::ESZ;
@@ -199,7 +202,8 @@ __global__ void __launch_bounds__(256) colmax_merge_kernel(const uint32_t *colpa
 template <int DT, int QB>
 __global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint32_t *colmax, int32_t *match_j,
                                                           float *match_s, int32_t *nn12, float *s12) {
-    resolve_block<DT, QB>(a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
+    __shared__ uint64_t red[256];
+    resolve_block<DT, QB, 256>(blockIdx.x, red, a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
                       [&](int x) { return a.Q + (long long)x * a.ld * Tr<DT>::ESZ; },
                       [&](bool valid, int x, int j, float s, int sub) {
                           if (valid && sub == 0) {
@@ -230,7 +234,9 @@ struct FrmState {
 // Seed grid (rows S/2 + S*n < H1, columns S/2 + S*n < W1, p = x + W1*y,
 // ascending) and the initial state; also clears the dense match array.
 __global__ void __launch_bounds__(256) frm_init_kernel(FrmState st, int k, int kx, int W1, int S, int N1,
-                                                       int nhalf) {
+                                                       int nhalf, uint32_t *ctl) {
+    // control words of the single-launch loop: barrier arrivals and error flag
+    if (ctl && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) ctl[threadIdx.x * 32] = 0;
     const int pair = blockIdx.y;
     const long long ko = pair * st.k_bs;
     for (int a = blockIdx.x * 256 + threadIdx.x; a < k; a += gridDim.x * 256) {
@@ -244,21 +250,23 @@ __global__ void __launch_bounds__(256) frm_init_kernel(FrmState st, int k, int k
         for (int h = threadIdx.x; h <= nhalf; h += 256) st.counts[pair * st.cnt_bs + h] = (h == 0) ? k : 0;
 }
 
-// One half-step's update: resolve each active query, apply the cycle test and
-// append the seeds that stay active to the next list (wave ballot + one atomic
-// per wave; list order does not affect any result). 16 queries per block.
-template <int DT>
-__global__ void __launch_bounds__(256) frm_update_kernel(ResolveArgs a, FrmState st, int h, int backward,
-                                                         int iter) {
-    const int pair = blockIdx.y;
+// One half-step's update for query block blk of pair `pair`: resolve each
+// active query, apply the cycle test and append the seeds that stay active to
+// the next list (wave ballot + one atomic per wave; list order does not affect
+// any result).
+template <int DT, int QB, int NT>
+__device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmState &st, int h, int backward,
+                                                int iter, int pair, int blk, uint64_t *red) {
     const int cur = h & 1, nxt = cur ^ 1;
     const long long ko = pair * st.k_bs;
     int32_t *counts = st.counts + pair * st.cnt_bs;
     const int nq = counts[h];
     const int lane = threadIdx.x & 63;
     const unsigned char *Q = a.Q + pair * a.q_bs;
-    resolve_block<DT, 16>(
-        a.rowpart + pair * a.rowpart_bs, a.nchunks, a.rowcap, nq, a.R + pair * a.r_bs, a.nref, a.ld, a.d,
+    const SplitGeom sg = split_geom(a.split, nq, a.split_rows, a.qblocks, a.chunk_groups, a.nchunks, a.rowcap);
+    resolve_block<DT, QB, NT>(
+        blk, red, a.rowpart + pair * a.rowpart_bs, a.nchunks * sg.s, sg.rowcap, nq, a.R + pair * a.r_bs, a.nref,
+        a.ld, a.d,
         [&](int x) { return Q + (long long)st.qrows[cur][ko + x] * a.ld * Tr<DT>::ESZ; },
         [&](bool valid, int x, int j, float s, int sub) {
             bool keep = false;
@@ -337,8 +345,9 @@ __global__ void __launch_bounds__(256) compact_count_kernel(const int32_t *match
     if (threadIdx.x == 0) blockcnt[pair * nblk + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
+// out_count = -1 when *err is set (a grid barrier of the loop kernel timed out).
 __global__ void __launch_bounds__(256) compact_scan_kernel(const int32_t *blockcnt, int32_t *blockoff, int nblk,
-                                                           int32_t *out_count, int capacity) {
+                                                           int32_t *out_count, int capacity, const int32_t *err) {
     const int pair = blockIdx.x;
     __shared__ int carry;
     __shared__ int wsum[4];
@@ -362,7 +371,7 @@ __global__ void __launch_bounds__(256) compact_scan_kernel(const int32_t *blockc
         if (threadIdx.x == 0) carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out_count[pair] = carry < capacity ? carry : capacity;
+    if (threadIdx.x == 0) out_count[pair] = (err && *err) ? -1 : (carry < capacity ? carry : capacity);
 }
 
 __global__ void __launch_bounds__(256) compact_scatter_kernel(const int32_t *match_j, const float *match_s,

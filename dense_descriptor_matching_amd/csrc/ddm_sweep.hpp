@@ -117,8 +117,29 @@ struct SweepArgs {
     int chunk;                   // references per chunk (multiple of GROUP)
     int nchunks;
     int sb_per_wg;               // query sub-blocks per workgroup
-    int rowcap;                  // rows per chunk slice of rowpart
+    int rowcap;                  // rows per chunk slice of rowpart (without split)
+    // Runtime split (used with a device query count): when the count leaves
+    // query blocks idle and the pair's busy workgroups fall short of `split`,
+    // each reference chunk is cut into s sub-chunks (whole index groups)
+    // handled by the idle blocks; partial slot chunk*s + sub.
+    int split;                   // workgroups per pair to aim for; 0 = off
+    int qblocks;                 // query blocks in the grid
+    int split_rows;              // query rows per query block
 };
+
+// Geometry of the runtime split for nq queries: blocks with work (need),
+// sub-chunks per chunk (s) and rows per partial slot (rowcap). The sweep and
+// the resolve of one half-step evaluate it on the same count.
+struct SplitGeom { int need, s, rowcap; };
+__device__ __forceinline__ SplitGeom split_geom(int split, int nq, int rows, int qblocks, int groups_per_chunk,
+                                                int nchunks, int rowcap) {
+    if (!split) return SplitGeom{qblocks, 1, rowcap};
+    const int need = max(1, (nq + rows - 1) / rows);
+    const int busy = need * nchunks;
+    const int want = (split + busy - 1) / busy;
+    const int s = max(1, min(want, min(qblocks / need, groups_per_chunk)));
+    return SplitGeom{need, s, need * rows};
+}
 
 // Row-partial key: high word = order-preserving key of the row maximum, low
 // word = ~(global group << 4 | slot): the u64 maximum prefers the larger score,
@@ -154,24 +175,32 @@ __device__ __forceinline__ uint32_t row16_min(uint32_t x) {
 
 // NP = pieces (of E elements) per stored row; 0 = runtime (fp32 path).
 // NKB = 32-wide (fp16/bf16) or 4-wide (fp32) K blocks.
+// One workgroup task: reference chunk chunk_id of pair `pair` against query
+// block qblk. The caller owns the LDS (at least sweep_lds bytes) and makes sure
+// no wave still reads it from a previous task.
 template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
-__global__ void __launch_bounds__(NW * 64)
-sweep_kernel(SweepArgs p)
+__device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chunk_id, int qblk, unsigned char *lds)
 {
     constexpr int G = group_tiles(DT), GROUP = TILE * G;
     using T = Tr<DT>;
     using raw = typename T::raw;
     constexpr int E = T::E, PS = T::PS, ESZ = T::ESZ;
     constexpr int SB_ROWS = NW * RQ * 16;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int pair = blockIdx.z, chunk_id = blockIdx.x, qblk = blockIdx.y;
     const int nq = p.qcount ? p.qcount[pair * p.qcount_bs] : p.nq;
+    const SplitGeom sg = split_geom(p.split, nq, p.split_rows, p.qblocks, p.chunk / GROUP, p.nchunks, p.rowcap);
+    int qb = qblk, sub = 0;
+    if (p.split) {
+        qb = qblk % sg.need;
+        sub = qblk / sg.need;
+        if (sub >= sg.s) return;
+    }
     const int n_sb = (nq + SB_ROWS - 1) / SB_ROWS;
-    const int sb_first = qblk * p.sb_per_wg;
+    const int sb_first = qb * p.sb_per_wg;
     if (sb_first >= n_sb) return;
     const int sb_last = min(sb_first + p.sb_per_wg, n_sb);
+    uint64_t *rp = p.rowpart + pair * p.rowpart_bs + (long long)(chunk_id * sg.s + sub) * sg.rowcap;
 
     const unsigned char *Q = p.Q + pair * p.q_bs;
     const unsigned char *R = p.R + pair * p.r_bs;
@@ -180,8 +209,15 @@ sweep_kernel(SweepArgs p)
     const int np = NP > 0 ? NP : p.ld / E;          // pieces per row
     const int TB = np * 16 * PS;                    // LDS bytes per tile
     const int nkb = NP > 0 ? NKB : (np + 3) / 4;    // K blocks in use
-    const int r0 = chunk_id * p.chunk;
-    const int nvalid = min(p.chunk, p.nref - r0);
+    const int gpc = p.chunk / GROUP;
+    const int g0 = gpc * sub / sg.s, g1 = gpc * (sub + 1) / sg.s;
+    const int r0 = chunk_id * p.chunk + g0 * GROUP;
+    const int nvalid = min((g1 - g0) * GROUP, p.nref - r0);
+    if (nvalid <= 0) {
+        // a sub-chunk past the last reference: its partials lose to every real one
+        for (int row = sb_first * SB_ROWS + tid; row < min(sb_last * SB_ROWS, nq); row += NW * 64) rp[row] = 0;
+        return;
+    }
     const int ngroups = (nvalid + GROUP - 1) / GROUP;
     const int nslots = ngroups * GROUP;
 
@@ -211,7 +247,7 @@ sweep_kernel(SweepArgs p)
         const int pc = min(kb * 4 + g, np - 1);     // lanes past the last piece re-read it; A is 0 there
         boff[kb] = pc * 16 * PS + c * PS;
     }
-    const uint32_t gbase = (uint32_t)chunk_id * (uint32_t)(p.chunk / GROUP);
+    const uint32_t gbase = (uint32_t)(r0 / GROUP);
 
     for (int sb = sb_first; sb < sb_last; ++sb) {
         const int row0 = sb * SB_ROWS + wave * RQ * 16;
@@ -367,7 +403,6 @@ sweep_kernel(SweepArgs p)
         }
 
         // ---- row flush: max over the 16 slots of each row, lowest (group, slot) among equals
-        uint64_t *rp = p.rowpart + pair * p.rowpart_bs + (long long)chunk_id * p.rowcap;
 #pragma unroll
         for (int qt = 0; qt < RQ; ++qt)
 #pragma unroll
@@ -390,6 +425,14 @@ sweep_kernel(SweepArgs p)
             if (r < nvalid) cp[r] = fkey(colmax_lds[s]);
         }
     }
+}
+
+template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
+__global__ void __launch_bounds__(NW * 64)
+sweep_kernel(SweepArgs p)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    sweep_task<DT, NP, NKB, RQ, NW, COLMAX>(p, blockIdx.z, blockIdx.x, blockIdx.y, lds);
 }
 
 }  // namespace ddm

@@ -98,7 +98,11 @@ int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, i
  *   query_counts             device int32[2*max_iter] or NULL: number of
  *                            forward / backward NN queries in each iteration
  *                            (entry 2t = forward, 2t+1 = backward of iteration t+1)
- * k = 0 (stride larger than the image) is valid and yields 0 pairs. */
+ * k = 0 (stride larger than the image) is valid and yields 0 pairs.
+ * out_count = -1 reports a failed device-wide synchronisation of the loop
+ * kernel (modes below); the other outputs are then undefined. Not expected in
+ * normal operation: that mode never launches more workgroups than the device
+ * keeps resident, and its barrier waits are bounded so the call always ends. */
 size_t ddm_frm_workspace_bytes(int B, int H1, int W1, int H2, int W2, int d, int dtype,
                                int grid_stride, int max_iter);
 int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
@@ -117,6 +121,24 @@ int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2,
                           int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* How FRM calls are executed (process-wide; results are identical):
+ *   DDM_FRM_PER_HALF_STEP (default): a sweep and an update launch for every
+ *     half-step of all max_iter iterations. Both kernels stride over the
+ *     active work only, so the half-steps after convergence cost a few
+ *     microseconds each.
+ *   DDM_FRM_LOOP: every iteration in one cooperative kernel that loops over
+ *     the half-steps with grid barriers and stops as soon as no seed is active
+ *     (the device must support cooperative launches, else per half-step).
+ *     Its barriers cost more than kernel boundaries on large maps; it pays off
+ *     on small ones.
+ * The launch sequence of a call is recorded once into a HIP graph, cached under
+ * the call's argument values and the mode, and replayed; on a stream that is
+ * being captured it is recorded into the caller's graph.
+ * ddm_frm_set_mode returns DDM_ERR_INVALID for other values. */
+typedef enum { DDM_FRM_PER_HALF_STEP = 0, DDM_FRM_LOOP = 1 } ddm_frm_mode;
+int ddm_frm_set_mode(int mode);
+int ddm_frm_get_mode(void);
+
 /* ---------------------------------------------------------- mutual NN ---
  * Exhaustive reciprocal nearest neighbours M (ascending in i), computed in a
  * single pass over all N1 x N2 scores with row arg-max and column max fused.
@@ -132,8 +154,9 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
 /* ------------------------------------------------------- kernel timing ---
  * Benchmark aid, off by default. ddm_profile_enable(mask) makes later calls
  * bracket each fused NN sweep launch with two HIP events on the call's stream:
- * mask bit 0 = the mutual-NN sweep, bit 1 = the NN / FRM sweeps, 0 = off (the
- * library then creates no events). ddm_profile_read waits for the recorded
+ * mask bit 0 = the mutual-NN sweep, bit 1 = the NN / FRM sweeps (and the FRM
+ * loop kernel as a whole), 0 = off (the library then creates no events). Bit 1
+ * also makes FRM calls launch directly instead of through the graph cache. ddm_profile_read waits for the recorded
  * events, returns the summed elapsed milliseconds and the number of launches,
  * and forgets them. Events are created on first use and kept for reuse. */
 int ddm_profile_enable(int mask);

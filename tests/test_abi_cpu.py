@@ -33,6 +33,14 @@ def test_header_symbols_exported(L):
         assert hasattr(L, n), f"{n} declared in ddm.h but not exported"
 
 
+def test_frm_mode_switch(L):
+    assert L.ddm_frm_get_mode() == 0                 # per half-step by default
+    assert L.ddm_frm_set_mode(1) == 0 and L.ddm_frm_get_mode() == 1
+    assert L.ddm_frm_set_mode(2) == -1 and L.ddm_frm_set_mode(-1) == -1
+    assert L.ddm_frm_get_mode() == 1                 # a rejected value changes nothing
+    assert L.ddm_frm_set_mode(0) == 0 and L.ddm_frm_get_mode() == 0
+
+
 def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5):
         assert L.ddm_status_str(code)

@@ -129,31 +129,103 @@ def test_determinism_full_size(ddm):
         assert torch.equal(x, y)
 
 
+def _frm_outputs(buf):
+    n = buf.count.cpu().numpy()
+    cap = buf.cap
+    outs = []
+    for b, nb in enumerate(n.tolist()):
+        assert nb >= 0
+        o = b * cap
+        outs.append((buf.out_i[o:o + nb].cpu().numpy(), buf.out_j[o:o + nb].cpu().numpy(),
+                     buf.out_s[o:o + nb].cpu().numpy()))
+    st = buf.state.cpu().numpy() if buf.state is not None else None
+    return n, outs, st, buf.qcounts.cpu().numpy()
+
+
+def _assert_same(a, b, what):
+    na, oa, sa, qa = a
+    nb, ob, sb, qb = b
+    assert np.array_equal(na, nb), what
+    for x, y in zip(oa, ob):
+        for u, v in zip(x, y):
+            assert np.array_equal(u, v), what
+    if sa is not None:
+        k = len(sa) // 4
+        assert np.array_equal(sa.reshape(-1, 4)[:, :3], sb.reshape(-1, 4)[:, :3]), what
+    assert np.array_equal(qa, qb), what
+
+
 def test_frm_graph_replays_match_direct_launches(ddm):
-    """FRM calls with unchanged arguments replay a cached HIP graph; every replay,
-    with unrelated work and host synchronisation in between, must equal a call made
-    with direct launches (sweep timing on forces those)."""
+    """Per-half-step FRM calls with unchanged arguments replay a cached HIP graph;
+    every replay, with unrelated work and host synchronisation in between, must
+    equal a call made with direct launches (sweep timing on forces those)."""
     import torch
     (p,) = synth.make_config("frm_512x384x24_f16")
     D1, D2 = dev(p.D1, p.dtype), dev(p.D2, p.dtype)
     buf = ddm.FrmBuffers(1, 512, 384, 512, 384, 24, torch.float16, 8, 10, D1.device)
-    ddm.profile_enable(2)
-    ddm.frm_match_into(D1, D2, 8, 10, buf)
-    torch.cuda.synchronize()
-    ddm.profile_read()
-    ddm.profile_enable(0)
-    ref = [t.clone() for t in (buf.out_i, buf.out_j, buf.out_s, buf.count, buf.state, buf.qcounts)]
-    for rep in range(4):
-        for t in (buf.out_i, buf.out_j, buf.state, buf.qcounts):
-            t.fill_(-7)
-        buf.out_s.fill_(float("nan")); buf.count.zero_()
-        x = torch.randn(1 << 20, device=D1.device).sum()      # unrelated work between replays
+    ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
+    try:
+        ddm.profile_enable(2)
         ddm.frm_match_into(D1, D2, 8, 10, buf)
         torch.cuda.synchronize()
-        got = (buf.out_i, buf.out_j, buf.out_s, buf.count, buf.state, buf.qcounts)
-        n = int(ref[3][0])
-        assert int(buf.count[0]) == n, f"replay {rep}"
-        for a, b in zip(got, ref):
-            assert torch.equal(a[: max(n, 1)] if a.numel() == ref[0].numel() else a,
-                               b[: max(n, 1)] if b.numel() == ref[0].numel() else b), f"replay {rep}"
-        del x
+        ddm.profile_read()
+        ddm.profile_enable(0)
+        ref = _frm_outputs(buf)
+        for rep in range(4):
+            for t in (buf.out_i, buf.out_j, buf.state, buf.qcounts):
+                t.fill_(-7)
+            buf.out_s.fill_(float("nan")); buf.count.zero_()
+            x = torch.randn(1 << 20, device=D1.device).sum()      # unrelated work between replays
+            ddm.frm_match_into(D1, D2, 8, 10, buf)
+            torch.cuda.synchronize()
+            _assert_same(_frm_outputs(buf), ref, f"replay {rep}")
+            del x
+    finally:
+        ddm.profile_enable(0)
+        ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
+
+
+FRM_MODE_CASES = [
+    # (config, stride, max_iter, batched)
+    ("tiny_frm_64x48x24_f32", 8, 10, False),
+    ("tiny_frm_64x48x24_f32", 3, 1, False),
+    ("frm_512x384x24_f16", 8, 10, False),
+    ("frm_512x384x24_f16", 8, 2, False),
+    ("frm_512x384x24_f16", 1000, 10, False),          # no seeds
+    ("batched_frm_16x512x384x24_f16", 8, 10, True),
+    ("hard_frm_512x512x64_bf16", 4, 20, False),
+]
+
+
+@pytest.mark.parametrize("name,S,it,batched", FRM_MODE_CASES)
+def test_frm_modes_agree(ddm, name, S, it, batched):
+    """Per-half-step launches and the loop kernel give the same bits: pairs,
+    scores, per-seed states and query counts; repeated calls on one workspace
+    agree too (the barrier counter restarts every call), and so do direct
+    launches (sweep timing on) and graph replays."""
+    import torch
+    pairs = synth.make_config(name)
+    D1 = torch.stack([dev(p.D1, p.dtype) for p in pairs]); D2 = torch.stack([dev(p.D2, p.dtype) for p in pairs])
+    if not batched:
+        D1, D2 = D1[0], D2[0]
+    p0 = pairs[0]
+    buf = ddm.FrmBuffers(len(pairs), p0.H1, p0.W1, p0.H2, p0.W2, p0.d, D1.dtype, S, it, D1.device)
+    runs = []
+    try:
+        for mode, timed in ((ddm.FRM_PER_HALF_STEP, True), (ddm.FRM_PER_HALF_STEP, False),
+                            (ddm.FRM_PER_HALF_STEP, False), (ddm.FRM_LOOP, False), (ddm.FRM_LOOP, False),
+                            (ddm.FRM_LOOP, True)):
+            ddm.frm_set_mode(mode)
+            ddm.profile_enable(2 if timed else 0)
+            buf.count.fill_(-3); buf.qcounts.fill_(-3); buf.state.fill_(-3)
+            ddm.frm_match_into(D1, D2, S, it, buf, batched=batched)
+            torch.cuda.synchronize()
+            ddm.profile_read()
+            runs.append(((mode, timed), _frm_outputs(buf)))
+    finally:
+        ddm.profile_enable(0)
+        ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
+    ref = runs[0][1]
+    for what, r in runs[1:]:
+        _assert_same(r, ref, f"{name} {what}")
+    print(f"{name} S={S} it={it}: counts={ref[0].tolist()[:4]} queries={ref[3].reshape(len(pairs), -1)[0][:8].tolist()}")
