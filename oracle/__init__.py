@@ -48,6 +48,10 @@ def _bind(path: str):
     lib.orc_seed_grid.restype = i64
     lib.orc_frm.argtypes = [P, i64, P, i64, i32, P, i64, i32, dbl, P, P, P, P, P, P, P, P]
     lib.orc_frm.restype = i32
+    lib.orc_frm_ex.argtypes = [P, i64, P, i64, i32, P, i64, i32, dbl, i32, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_frm_ex.restype = i32
+    lib.orc_frm_select.argtypes = [P, P, P, i64, i32, dbl, i32, P, P]
+    lib.orc_frm_select.restype = None
     lib.orc_merge.argtypes = [P, P, P, P, i64, P, P, P]
     lib.orc_merge.restype = i64
     lib.orc_mutual.argtypes = [P, i64, P, i64, i32, P, P, P, P, P, P, P, P, P]
@@ -155,6 +159,65 @@ def frm(D1: np.ndarray, D2: np.ndarray, seeds: np.ndarray, max_iter: int, tau: f
     return dict(u=u, v=v, score=score, conv_iter=conv, active=active.astype(bool),
                 ambiguous=amb.astype(bool), i=oi[:n].copy(), j=oj[:n].copy(), s=os_[:n].copy(),
                 niter=int(niter), n_fwd=nf[:max_iter], n_bwd=nb[:max_iter])
+
+
+def frm_ex(D1: np.ndarray, D2: np.ndarray, H1: int, W1: int, *, grid_stride: int | None = None,
+           starts: np.ndarray | None = None, max_iter: int = 10, pixel_tol: float = 0.0, ret_basin: bool = False,
+           tau: float = 1e-4):
+    """The FRM routine with its options ("DUSt3R和MASt3R论文阅读", section MASt3R matching, the quoted
+    fast_reciprocal_NNs routine):
+
+    - seeds: the stride grid (``grid_stride``) or the given image-1 pixels (``starts``, linear
+      p = x + W1*y), made unique and ascending;
+    - ``pixel_tol == 0``: a seed is kept when it is no longer active at exit; its pair is (u, v);
+    - ``pixel_tol > 0`` (given starts only; the routine has no grid form of it): a seed is kept when
+      the Euclidean pixel distance between u_old, as the loop leaves it, and u is below pixel_tol; the
+      reported image-1 pixel is u_old (the start itself in a one-iteration call);
+    - ``ret_basin``: the forward test is off and basin[p] (N1 entries, -1 elsewhere) records, for each
+      backward query, where a seed that stood at p moved to.
+
+    Returns a dict with the per-seed state (seeds, u, v, u_old, score, conv_iter, active, ambiguous),
+    the unique pairs i, j, s ascending in (i, j), basin (or None), niter, n_fwd, n_bwd."""
+    lib = _load()
+    A, B = _rows(D1), _rows(D2)
+    N1 = A.shape[0]
+    if N1 != H1 * W1:
+        raise ValueError("D1 does not hold H1 x W1 rows")
+    if (grid_stride is None) == (starts is None):
+        raise ValueError("give exactly one of grid_stride and starts")
+    if pixel_tol > 0 and starts is None:
+        raise ValueError("pixel_tol > 0 needs explicit starts")
+    if starts is not None:
+        st = np.asarray(starts, dtype=np.int64).ravel()
+        if st.size and (st.min() < 0 or st.max() >= N1):
+            raise ValueError("start outside image 1")
+        seeds = np.unique(st).astype(np.int32)
+    else:
+        seeds = seed_grid(H1, W1, grid_stride)
+    k = seeds.size
+    u = np.empty(k, np.int32); v = np.empty(k, np.int32); u_old = np.empty(k, np.int32)
+    score = np.empty(k, np.float64); conv = np.empty(k, np.int32)
+    active = np.empty(k, np.uint8); amb = np.empty(k, np.uint8)
+    nf = np.zeros(max(max_iter, 1), np.int64); nb = np.zeros(max(max_iter, 1), np.int64)
+    basin = np.full(N1, -1, np.int32) if ret_basin else None
+    niter = lib.orc_frm_ex(_p(A), N1, _p(B), B.shape[0], A.shape[1], _p(seeds), k, max_iter, tau,
+                           0 if ret_basin else 1, _p(basin) if ret_basin else None, _p(u_old),
+                           _p(u), _p(v), _p(score), _p(conv), _p(active), _p(amb), _p(nf), _p(nb))
+    if niter < 0:
+        raise MemoryError
+    act = active.astype(bool)
+    keep = np.empty(k, np.uint8); rep_i = np.empty(k, np.int32)
+    lib.orc_frm_select(_p(u), _p(u_old), _p(active), k, W1, float(pixel_tol), 1 if starts is not None else 0,
+                       _p(keep), _p(rep_i))
+    keep = keep.astype(bool)
+    pi, pj, ps = rep_i[keep], v[keep], score[keep]
+    order = np.lexsort((pj, pi))
+    pi, pj, ps = pi[order], pj[order], ps[order]
+    first = np.ones(pi.size, bool)
+    first[1:] = (pi[1:] != pi[:-1]) | (pj[1:] != pj[:-1])
+    return dict(seeds=seeds, u=u, v=v, u_old=u_old, score=score, conv_iter=conv, active=act,
+                ambiguous=amb.astype(bool), i=pi[first].copy(), j=pj[first].copy(), s=ps[first].copy(),
+                basin=basin, niter=int(niter), n_fwd=nf[:max_iter], n_bwd=nb[:max_iter])
 
 
 def mutual(D1: np.ndarray, D2: np.ndarray):

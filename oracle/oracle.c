@@ -150,11 +150,26 @@ int64_t orc_seed_grid(int H, int W, int S, int32_t *out)
  * active (-1 if never); ambiguous[a] = 1 if any query on a's path had a
  * margin below tau; n_fwd[t] / n_bwd[t] (when not NULL, max_iter entries) =
  * number of forward / backward queries made in iteration t + 1, i.e. the work
- * the loop does. Returns the number of iterations run. */
-int orc_frm(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
-            const int32_t *seeds, int64_t k, int max_iter, double tau,
-            int32_t *u, int32_t *v, double *score, int32_t *conv_iter,
-            uint8_t *active, uint8_t *ambiguous, int64_t *n_fwd, int64_t *n_bwd)
+ * the loop does. Returns the number of iterations run.
+ *
+ * Options of the same routine [FRM-listing]:
+ *   fwd_test = 0  (the basin variant): the forward test is skipped, so a seed
+ *                 only stops when its backward query returns the pixel it
+ *                 started the iteration from;
+ *   basin         (NULL or int32[N1], filled with -1 by the caller): every
+ *                 backward query of an active seed records, at the pixel the
+ *                 seed occupied before the query (u_old), the pixel it moved
+ *                 to;
+ *   u_old_out     (NULL or int32[k]): the u_old copies as they stand when the
+ *                 loop ends -- u at the start of the last iteration if the
+ *                 loop stopped at max_iter, the final u if it stopped because
+ *                 no seed was active (the copy is refreshed after every
+ *                 iteration that does not hit max_iter). */
+int orc_frm_ex(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
+               const int32_t *seeds, int64_t k, int max_iter, double tau, int fwd_test,
+               int32_t *basin, int32_t *u_old_out,
+               int32_t *u, int32_t *v, double *score, int32_t *conv_iter,
+               uint8_t *active, uint8_t *ambiguous, int64_t *n_fwd, int64_t *n_bwd)
 {
     int32_t *u_old = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k ? k : 1));
     int32_t *v_old = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k ? k : 1));
@@ -185,7 +200,7 @@ int orc_frm(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
             if (s1 - s2 < tau) ambiguous[a] = 1;
         }
         for (int64_t a = 0; a < k; ++a)
-            if (active[a] && v[a] == v_old[a]) { active[a] = 0; conv_iter[a] = niter + 1; }
+            if (fwd_test && active[a] && v[a] == v_old[a]) { active[a] = 0; conv_iter[a] = niter + 1; }
 
         /* backward queries: image 2 -> image 1 */
         if (n_bwd)
@@ -198,6 +213,9 @@ int orc_frm(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
             u[a] = i;
             if (s1 - s2 < tau) ambiguous[a] = 1;
         }
+        if (basin)
+            for (int64_t a = 0; a < k; ++a)
+                if (active[a]) basin[u_old[a]] = u[a];
         for (int64_t a = 0; a < k; ++a)
             if (active[a] && u[a] == u_old[a]) { active[a] = 0; conv_iter[a] = niter + 1; }
 
@@ -205,8 +223,43 @@ int orc_frm(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
         if (niter >= max_iter) break;
         for (int64_t a = 0; a < k; ++a) { v_old[a] = v[a]; u_old[a] = u[a]; }
     }
+    if (u_old_out)
+        for (int64_t a = 0; a < k; ++a) u_old_out[a] = u_old[a];
     free(u_old); free(v_old);
     return niter;
+}
+
+/* The grid-seed routine with its defaults: forward test on, no basin. */
+int orc_frm(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
+            const int32_t *seeds, int64_t k, int max_iter, double tau,
+            int32_t *u, int32_t *v, double *score, int32_t *conv_iter,
+            uint8_t *active, uint8_t *ambiguous, int64_t *n_fwd, int64_t *n_bwd)
+{
+    return orc_frm_ex(D1, N1, D2, N2, d, seeds, k, max_iter, tau, 1, NULL, NULL, u, v, score, conv_iter, active,
+                      ambiguous, n_fwd, n_bwd);
+}
+
+/* Which seeds the routine keeps, and the image-1 pixel it reports for each
+ * [FRM-listing, end of the routine]:
+ *   pixel_tol == 0: kept = not active at exit; reported pixel = u;
+ *   pixel_tol >  0: kept = the Euclidean distance, in pixels of the W1-wide
+ *                   image, between u_old (as the loop left it) and u is below
+ *                   pixel_tol; reported pixel = u_old when report_old (seeds
+ *                   given as explicit starts), else u. */
+void orc_frm_select(const int32_t *u, const int32_t *u_old, const uint8_t *active, int64_t k, int W1,
+                    double pixel_tol, int report_old, uint8_t *keep, int32_t *rep_i)
+{
+    for (int64_t a = 0; a < k; ++a) {
+        if (pixel_tol > 0) {
+            const double dy = (double)(u_old[a] / W1 - u[a] / W1);
+            const double dx = (double)(u_old[a] % W1 - u[a] % W1);
+            keep[a] = sqrt(dy * dy + dx * dx) < pixel_tol;
+            rep_i[a] = report_old ? u_old[a] : u[a];
+        } else {
+            keep[a] = !active[a];
+            rep_i[a] = u[a];
+        }
+    }
 }
 
 static int cmp_pair(const void *pa, const void *pb)

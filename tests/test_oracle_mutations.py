@@ -29,9 +29,10 @@ MUTATIONS = {
     "half_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     "seed_offset_zero": ("for (int y = S / 2; y < H; y += S)", "for (int y = 0; y < H; y += S)"),
     "seed_index_transposed": ("if (out) out[k] = x + W * y;", "if (out) out[k] = y + H * x;"),
-    "forward_test_vs_u": ("if (active[a] && v[a] == v_old[a])", "if (active[a] && v[a] == u_old[a])"),
+    "forward_test_vs_u": ("if (fwd_test && active[a] && v[a] == v_old[a])",
+                          "if (fwd_test && active[a] && v[a] == u_old[a])"),
     "backward_test_vs_v": ("if (active[a] && u[a] == u_old[a])", "if (active[a] && u[a] == v_old[a])"),
-    "no_forward_test": ("if (active[a] && v[a] == v_old[a])", "if (0 && v[a] == v_old[a])"),
+    "no_forward_test": ("if (fwd_test && active[a] && v[a] == v_old[a])", "if (0 && v[a] == v_old[a])"),
     "max_iter_off_by_one": ("if (niter >= max_iter) break;", "if (niter > max_iter) break;"),
     "old_not_updated": ("for (int64_t a = 0; a < k; ++a) { v_old[a] = v[a]; u_old[a] = u[a]; }",
                         "for (int64_t a = 0; a < k; ++a) { v_old[a] = v[a]; }"),
@@ -40,6 +41,15 @@ MUTATIONS = {
     "forward_query_from_wrong_map": ("nn_one(D1 + (int64_t)u[a] * d, D2, N2, d, &j, &s1, &s2);",
                                      "nn_one(D2 + (int64_t)u[a] * d, D2, N2, d, &j, &s1, &s2);"),
     "converged_keeps_active": ("if (active[a]) continue;\n        buf[3 * m]", "if (!active[a]) continue;\n        buf[3 * m]"),
+    "basin_at_new_pixel": ("if (active[a]) basin[u_old[a]] = u[a];", "if (active[a]) basin[u[a]] = u[a];"),
+    "u_old_export_is_u": ("u_old_out[a] = u_old[a];", "u_old_out[a] = u[a];"),
+    "fwd_test_flag_ignored": ("if (fwd_test && active[a] && v[a] == v_old[a])",
+                              "if (active[a] && v[a] == v_old[a])"),
+    "tol_not_strict": ("keep[a] = sqrt(dy * dy + dx * dx) < pixel_tol;",
+                       "keep[a] = sqrt(dy * dy + dx * dx) <= pixel_tol;"),
+    "tol_reports_new_pixel": ("rep_i[a] = report_old ? u_old[a] : u[a];", "rep_i[a] = u[a];"),
+    "tol_distance_ignores_rows": ("const double dy = (double)(u_old[a] / W1 - u[a] / W1);",
+                                  "const double dy = 0.0;"),
     "mutual_check_wrong_table": ("if (nn21[j] == (int32_t)i) {", "if (nn12[j] == (int32_t)i) {"),
     "mutual_score_wrong": ("out_s[n] = s12[i];", "out_s[n] = s21[i];"),
 }
@@ -60,6 +70,11 @@ PINS = [
     lambda: P.test_frm_pure_shift_closed_form(3, 2),
     lambda: P.test_mutual_matches_numpy((7, 9), (11, 5), 3, 52),
     P.test_mutual_symmetry,
+] + [(lambda c=c: P.test_frm_ex_handworked_fixture(c)) for c in range(8)] + [
+    lambda: P.test_frm_ex_equals_orbit_derivation((6, 10), 2, 62, 3, 0.0, True),
+    lambda: P.test_frm_ex_equals_orbit_derivation((12, 9), 24, 63, 2, 2.5, False),
+    lambda: P.test_frm_ex_equals_orbit_derivation((1, 40), 2, 64, 10, 1.0, False),
+    P.test_frm_ex_identity_and_shift_closed_forms,
 ]
 
 

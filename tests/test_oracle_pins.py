@@ -263,6 +263,132 @@ def test_frm_no_seeds_and_empty_maps():
     assert oracle.seed_grid(2, 2, 5).size == 0
 
 
+# ------------------------------------------------- FRM options: starts, pixel_tol, basin
+@pytest.mark.parametrize("case", range(8))
+def test_frm_ex_handworked_fixture(case):
+    g = _gold("frm_starts_tol_basin.json")
+    c = g["cases"][case]
+    A = _angle_map(g["D1_degrees"]).reshape(g["H1"], g["W1"], 2)
+    B = _angle_map(g["D2_degrees"]).reshape(g["H2"], g["W2"], 2)
+    r = oracle.frm_ex(A, B, g["H1"], g["W1"], starts=np.array(g["starts"]), max_iter=c["max_iter"],
+                      pixel_tol=c["pixel_tol"], ret_basin=c["ret_basin"])
+    assert r["seeds"].tolist() == sorted(set(g["starts"])), c["name"]
+    for key in ("u", "v", "u_old", "conv_iter", "n_fwd", "n_bwd"):
+        assert r[key].tolist() == c[key], (c["name"], key, r[key].tolist())
+    assert [list(p) for p in zip(r["i"].tolist(), r["j"].tolist())] == c["pairs"], c["name"]
+    if c["ret_basin"]:
+        assert r["basin"].tolist() == c["basin"], c["name"]
+    else:
+        assert r["basin"] is None
+
+
+def _orbit_ex_expectation(A, B, W1, seeds, max_iter, pixel_tol, explicit, basin_mode):
+    """Independent derivation of the optioned routine from the NN tables (numpy argmax) and
+    the orbit of f = NN1 o NN2: seed s sits at u_t = f^t(s) after t backward steps and
+    stops in iteration m_s + 1 (m_s = first t with f(u_t) = u_t) whichever test is on;
+    the loop runs iteration max_iter iff some seed is still active when it starts, and
+    then u_old = u at its start, else u_old = final u; the basin records f(u_t) at u_t for
+    every backward step taken."""
+    nn12 = _np_nn(A, B)[0]; nn21 = _np_nn(B, A)[0]
+    f = nn21[nn12]
+    N1 = len(nn12)
+    traj, stop = [], []
+    for s in seeds:
+        t = [int(s)]
+        m = None
+        for step in range(max_iter):
+            nxt = int(f[t[-1]])
+            if nxt == t[-1]:
+                m = step
+                break
+            t.append(nxt)
+        traj.append(t)
+        stop.append(m + 1 if m is not None else None)      # iteration in which the seed stops
+    reached_last = any(st is None or st >= max_iter for st in stop)
+    out = dict(u=[], v=[], u_old=[], conv=[], basin=np.full(N1, -1, np.int64), pairs=set())
+    for t, st in zip(traj, stop):
+        final_u = t[-1]
+        last_fwd_from = t[-1] if st is not None else t[-2]
+        v = int(nn12[last_fwd_from])
+        u_old = t[min(len(t) - 1, max_iter - 1)] if reached_last else final_u
+        out["u"].append(final_u); out["v"].append(v); out["u_old"].append(u_old)
+        out["conv"].append(st if st is not None else -1)
+        n_bwd_steps = min(st if st is not None else max_iter, max_iter)
+        if basin_mode:
+            for q in range(n_bwd_steps):
+                out["basin"][t[q]] = int(f[t[q]])
+        if pixel_tol > 0:
+            dy, dx = u_old // W1 - final_u // W1, u_old % W1 - final_u % W1
+            if (dy * dy + dx * dx) ** 0.5 < pixel_tol:
+                out["pairs"].add((u_old if explicit else final_u, v))
+        elif st is not None:
+            out["pairs"].add((final_u, v))
+    return out
+
+
+@pytest.mark.parametrize("shape,d,seed", [((8, 8), 3, 61), ((6, 10), 2, 62), ((12, 9), 24, 63), ((1, 40), 2, 64)])
+@pytest.mark.parametrize("max_iter", [1, 2, 3, 10])
+@pytest.mark.parametrize("pixel_tol,basin", [(0.0, False), (0.0, True), (1.0, False), (2.5, False), (1.5, True)])
+def test_frm_ex_equals_orbit_derivation(shape, d, seed, max_iter, pixel_tol, basin):
+    H1, W1 = shape
+    A = synth.random_map(H1, W1, d, synth.F16, seed).astype(np.float64)
+    B = synth.random_map(W1, H1, d, synth.F16, seed + 1).astype(np.float64)
+    rng = np.random.default_rng(seed)
+    starts = rng.integers(0, H1 * W1, size=H1 * W1 // 2 + 3)          # duplicates on purpose
+    r = oracle.frm_ex(A, B, H1, W1, starts=starts, max_iter=max_iter, pixel_tol=pixel_tol, ret_basin=basin)
+    seeds = np.unique(starts)
+    assert np.array_equal(r["seeds"], seeds)
+    exp = _orbit_ex_expectation(A, B, W1, seeds, max_iter, pixel_tol, True, basin)
+    assert r["u"].tolist() == exp["u"] and r["v"].tolist() == exp["v"]
+    assert r["u_old"].tolist() == exp["u_old"] and r["conv_iter"].tolist() == exp["conv"]
+    assert list(zip(r["i"].tolist(), r["j"].tolist())) == sorted(exp["pairs"])
+    if basin:
+        assert r["basin"].tolist() == exp["basin"].tolist()
+
+
+def test_frm_ex_grid_matches_plain_routine():
+    A = synth.random_map(16, 12, 8, synth.F16, 71).astype(np.float64)
+    B = synth.random_map(14, 12, 8, synth.F16, 72).astype(np.float64)
+    for it in (1, 3, 10):
+        a = oracle.frm_ex(A, B, 16, 12, grid_stride=3, max_iter=it)
+        b = oracle.frm(A, B, oracle.seed_grid(16, 12, 3), it)
+        for key in ("u", "v", "conv_iter", "i", "j", "n_fwd", "n_bwd"):
+            assert np.array_equal(a[key], b[key]), key
+
+
+def test_frm_ex_identity_and_shift_closed_forms():
+    # identity: every start is its own reciprocal pair, its basin entry is itself
+    p = synth.make_pair(12, 10, 24, synth.F16, 73, sigma=0.0, shift=(0, 0))
+    A = oracle.decode(p.D1, oracle.F16); B = oracle.decode(p.D2, oracle.F16)
+    starts = np.array([5, 5, 17, 3, 119, 60])
+    for tol in (0.0, 0.5):
+        r = oracle.frm_ex(A, B, 12, 10, starts=starts, max_iter=1, pixel_tol=tol, ret_basin=True)
+        u = np.unique(starts)
+        assert r["i"].tolist() == u.tolist() and r["j"].tolist() == u.tolist()
+        exp_basin = np.full(120, -1); exp_basin[u] = u
+        assert r["basin"].tolist() == exp_basin.tolist()
+    # pure shift: a start whose counterpart is in range maps to p - dx - dy*W in one round trip
+    dx, dy, H, W = 3, -2, 14, 11
+    p = synth.make_pair(H, W, 24, synth.F16, 74, sigma=0.0, shift=(dx, dy))
+    A = oracle.decode(p.D1, oracle.F16); B = oracle.decode(p.D2, oracle.F16)
+    inside = [q for q in range(H * W) if 0 <= q % W - dx < W and 0 <= q // W - dy < H]
+    r = oracle.frm_ex(A, B, H, W, starts=np.array(inside), max_iter=1, pixel_tol=0.5)
+    assert r["i"].tolist() == inside
+    assert r["j"].tolist() == [q - dx - dy * W for q in inside]
+
+
+def test_frm_ex_rejects_undefined_requests():
+    A = synth.random_map(4, 4, 3, synth.F32, 75).astype(np.float64)
+    with pytest.raises(ValueError):
+        oracle.frm_ex(A, A, 4, 4, grid_stride=2, pixel_tol=1.0)       # the routine has no grid form of it
+    with pytest.raises(ValueError):
+        oracle.frm_ex(A, A, 4, 4, starts=np.array([16]))
+    with pytest.raises(ValueError):
+        oracle.frm_ex(A, A, 4, 4)
+    r = oracle.frm_ex(A, A, 4, 4, starts=np.zeros(0, np.int64), max_iter=1)
+    assert r["i"].size == 0
+
+
 # --------------------------------------------------------------------- mutual
 @pytest.mark.parametrize("s1,s2,d,seed", [((10, 12), (10, 12), 24, 51), ((7, 9), (11, 5), 3, 52),
                                           ((16, 16), (16, 16), 2, 53)])
