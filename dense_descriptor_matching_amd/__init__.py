@@ -53,6 +53,11 @@ def _declare(lib):
     lib.ddm_mutual_workspace_bytes.argtypes = [I, I, I, I, I, I]; lib.ddm_mutual_workspace_bytes.restype = SZ
     lib.ddm_mutual_nn.argtypes = [P, I, I, P, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
     lib.ddm_mutual_nn.restype = I
+    lib.ddm_frm_ex_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
+    lib.ddm_frm_ex_workspace_bytes.restype = SZ
+    lib.ddm_frm_match_ex.argtypes = [P, I, I, P, I, I, I, I, I, P, I, I, C.c_double, P,
+                                     P, P, P, I, P, P, P, P, SZ, P]
+    lib.ddm_frm_match_ex.restype = I
     lib.ddm_frm_set_mode.argtypes = [I]; lib.ddm_frm_set_mode.restype = I
     lib.ddm_frm_get_mode.argtypes = []; lib.ddm_frm_get_mode.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
@@ -249,6 +254,70 @@ def frm_match_batched(D1: torch.Tensor, D2: torch.Tensor, grid_stride: int = 8, 
     return out
 
 
+def frm_match_ex(D1: torch.Tensor, D2: torch.Tensor, *, grid_stride: int = 8, starts=None,
+                 max_iter: int | None = None, pixel_tol: float = 0.0, ret_basin: bool = False,
+                 return_state: bool = False):
+    """FRM with the routine's options (explicit starts, pixel tolerance, basin map); one pair.
+
+    ``starts``: None for the stride grid; an int tensor of linear image-1 pixels (p = x + W1*y);
+    or a pair (x, y) of int tensors. Entries outside image 1 are ignored, the rest are made
+    unique and ascending. ``max_iter`` defaults to 1 with starts (the routine's value) and 10
+    on the grid. ``pixel_tol > 0`` needs starts: a seed is kept when its image-1 pixel moved by
+    less than pixel_tol over the last iteration, and is reported at its pixel before that
+    iteration. ``ret_basin`` turns the forward test off and returns basin [H1*W1] int32
+    (where a backward query from each pixel went, -1 if none).
+
+    Returns (i, j, score) [+ basin] [+ dict(state=[k, 4] (u, v, conv_iter, u_old), query_counts)]."""
+    _check_map(D1, "D1"); _check_map(D2, "D2")
+    if D1.dtype != D2.dtype or D1.shape[-1] != D2.shape[-1] or D1.dim() != 3 or D2.dim() != 3:
+        raise ValueError("D1, D2 must be [H, W, d] maps of one dtype and d")
+    H1, W1, d = D1.shape
+    H2, W2, _ = D2.shape
+    dev = D1.device
+    if starts is not None:
+        if isinstance(starts, (tuple, list)):
+            x, y = starts
+            starts = torch.as_tensor(x, device=dev).long() + W1 * torch.as_tensor(y, device=dev).long()
+        starts = torch.as_tensor(starts, device=dev).to(torch.int32).contiguous().view(-1)
+        n = starts.numel()
+        if n == 0:                     # a null list would select the grid: pass a real pointer
+            starts = torch.zeros(1, dtype=torch.int32, device=dev)
+        if max_iter is None:
+            max_iter = 1
+    else:
+        n = -1
+        if max_iter is None:
+            max_iter = 10
+    L = lib()
+    dt = _DT[D1.dtype]
+    k = n if n >= 0 else seed_count(H1, W1, grid_stride)
+    cap = max(k, 1)
+    out_i = torch.empty(cap, dtype=torch.int32, device=dev)
+    out_j = torch.empty(cap, dtype=torch.int32, device=dev)
+    out_s = torch.empty(cap, dtype=torch.float32, device=dev)
+    count = torch.zeros(1, dtype=torch.int32, device=dev)
+    state = torch.empty(cap * 4, dtype=torch.int32, device=dev) if return_state else None
+    qc = torch.zeros(2 * max_iter, dtype=torch.int32, device=dev) if return_state else None
+    basin = torch.empty(H1 * W1, dtype=torch.int32, device=dev) if ret_basin else None
+    nbytes = L.ddm_frm_ex_workspace_bytes(H1, W1, H2, W2, d, dt, grid_stride, n, max_iter)
+    if nbytes == 0:
+        raise DDMError(-1, "ddm_frm_ex_workspace_bytes")
+    ws = _workspace(nbytes, dev)
+    _rc(L.ddm_frm_match_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride,
+                           _ptr(starts) if n >= 0 else None, max(n, 0), max_iter, float(pixel_tol), _ptr(basin),
+                           _ptr(out_i), _ptr(out_j), _ptr(out_s), cap, _ptr(count), _ptr(state), _ptr(qc),
+                           _ptr(ws), ws.numel(), _stream()), "ddm_frm_match_ex")
+    m = _count(count[0].item())
+    res = (out_i[:m].clone(), out_j[:m].clone(), out_s[:m].clone())
+    if ret_basin:
+        res = res + (basin,)
+    if return_state:
+        # seeds = distinct valid starts: the forward queries of the first iteration
+        kk = int(qc[0].item()) if n >= 0 else k
+        res = res + (dict(state=state.view(-1, 4)[:kk].clone(), query_counts=qc.clone()),)
+    return res
+
+
 # ------------------------------------------------------------------- mutual NN
 class MutualBuffers:
     def __init__(self, H1, W1, H2, W2, d, dtype, device, with_nn=False):
@@ -291,6 +360,6 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False):
     return res
 
 
-__all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "mutual_nn", "mutual_nn_into", "seed_count",
+__all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "mutual_nn", "mutual_nn_into", "seed_count",
            "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH", "profile_enable", "profile_read",
            "frm_set_mode", "frm_get_mode", "FRM_PER_HALF_STEP", "FRM_LOOP"]

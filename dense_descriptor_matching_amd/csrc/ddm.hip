@@ -6,6 +6,7 @@
 #include "ddm_frm.hpp"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <array>
@@ -362,8 +363,18 @@ struct FrmPlan {
     int chunk1, chunk2, nch1, nch2, qblocks, nblk;
     long long k_bs, cnt_bs, part_bs;
     size_t o_u, o_v, o_conv, o_score, o_act0, o_act1, o_qr0, o_qr1, o_counts, o_part, o_mj, o_ms, o_bc, o_bo,
-        o_r1, o_r2, o_ctl, total;
+        o_r1, o_r2, o_ctl, o_uprev, o_uiter, o_marks, total;
     size_t loop_lds;       // dynamic LDS of the loop kernel
+    bool explicit_starts;  // seeds from a caller list (k = its length, an upper bound) instead of the grid
+};
+
+// Options of the routine beyond the grid form: explicit start pixels, the pixel
+// tolerance of the final selection, and the basin variant.
+struct FrmOpts {
+    const int32_t *starts = nullptr;   // device int32[n_starts] linear image-1 pixels, or null for the grid
+    int n_starts = 0;
+    double pixel_tol = 0.0;
+    int32_t *basin = nullptr;          // device int32[N1], or null
 };
 
 int frm_chunk(const MapFmt &f, int nref, long long wg_other) {
@@ -372,15 +383,25 @@ int frm_chunk(const MapFmt &f, int nref, long long wg_other) {
     return chunk;
 }
 
-int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int max_iter, FrmPlan *p) {
+// n_starts < 0: seeds on the stride-S grid; n_starts >= 0: that many explicit starts (one pair only).
+int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int max_iter, FrmPlan *p,
+             int n_starts = -1) {
     if (B < 1 || !pix_ok(H1, W1) || !pix_ok(H2, W2)) return DDM_ERR_INVALID;
-    if (S < 1 || max_iter < 1 || max_iter > DDM_MAX_ITER) return DDM_ERR_INVALID;
+    if (max_iter < 1 || max_iter > DDM_MAX_ITER) return DDM_ERR_INVALID;
+    if (n_starts < 0 && S < 1) return DDM_ERR_INVALID;
+    if (n_starts >= 0 && (B != 1 || n_starts > MAX_PIX)) return DDM_ERR_INVALID;
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
     if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
     p->B = B; p->H1 = H1; p->W1 = W1; p->N1 = H1 * W1; p->N2 = H2 * W2;
-    p->S = S; p->max_iter = max_iter; p->nhalf = 2 * max_iter;
-    p->k = (int)seed_count(H1, W1, S);
-    p->kx = W1 > S / 2 ? (W1 - S / 2 + S - 1) / S : 0;
+    p->max_iter = max_iter; p->nhalf = 2 * max_iter;
+    p->explicit_starts = n_starts >= 0;
+    if (p->explicit_starts) {
+        p->S = 1; p->k = n_starts; p->kx = 0;
+    } else {
+        p->S = S;
+        p->k = (int)seed_count(H1, W1, S);
+        p->kx = W1 > S / 2 ? (W1 - S / 2 + S - 1) / S : 0;
+    }
     const int sbr = p->f.sb_rows();
     const int kk = std::max(p->k, 1);
     p->qblocks = (kk + sbr - 1) / sbr;
@@ -406,6 +427,8 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
     p->o_r1 = p->f.repack ? b.take((size_t)B * p->N1 * p->f.ld * 2) : 0;
     p->o_r2 = p->f.repack ? b.take((size_t)B * p->N2 * p->f.ld * 2) : 0;
     p->o_ctl = b.take(256);
+    p->o_uprev = b.take(kb); p->o_uiter = b.take(kb);
+    p->o_marks = p->explicit_starts ? b.take((size_t)p->N1 * 4) : 0;
     p->total = b.off;
     p->loop_lds = std::max(sweep_lds(p->f, std::max(p->chunk1, p->chunk2), false),
                            (size_t)nw_for(dtype) * 64 * sizeof(uint64_t));
@@ -458,9 +481,9 @@ void frm_dir_args(const FrmPlan &P, const void *m1, const void *m2, uint64_t *pa
 // Half-steps [0, h_loop) run as one sweep and one update launch each, the
 // rest (all of them in the loop mode) in one cooperative loop kernel that
 // stops when no seed is active. The whole sequence can be captured into a graph.
-int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, int32_t *out_j, float *out_score,
-            int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *ws,
-            hipStream_t s, int h_loop) {
+int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, int32_t *out_i, int32_t *out_j,
+            float *out_score, int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
+            void *ws, hipStream_t s, int h_loop) {
     unsigned char *w = (unsigned char *)ws;
     const MapFmt &f = P.f;
     const void *m1, *m2;
@@ -476,14 +499,28 @@ int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, in
     st.qrows[0] = (int32_t *)(w + P.o_qr0); st.qrows[1] = (int32_t *)(w + P.o_qr1);
     st.counts = (int32_t *)(w + P.o_counts);
     st.match_j = (int32_t *)(w + P.o_mj); st.match_s = (float *)(w + P.o_ms);
+    st.uprev = (int32_t *)(w + P.o_uprev); st.uiter = (int32_t *)(w + P.o_uiter);
+    st.basin = O.basin;
     st.k_bs = P.k_bs; st.cnt_bs = P.cnt_bs; st.n1_bs = P.N1;
     uint64_t *part = (uint64_t *)(w + P.o_part);
     uint32_t *ctl = (uint32_t *)(w + P.o_ctl);
+    int32_t *marks = P.explicit_starts ? (int32_t *)(w + P.o_marks) : nullptr;
 
     const int init_blocks = (int)std::min<long long>((std::max(P.k, P.N1) + 255) / 256, 4096);
     hipLaunchKernelGGL(frm_init_kernel, dim3(init_blocks, P.B), dim3(256), 0, s, st, P.k, std::max(P.kx, 1),
-                       P.W1, P.S, P.N1, P.nhalf, ctl);
+                       P.W1, P.S, P.N1, P.nhalf, ctl, marks);
     DDM_CHECK_LAUNCH();
+    if (P.explicit_starts && P.k > 0) {
+        // distinct starts, ascending: marks -> ordered compaction into u / qrows[0], count into counts[0]
+        const int mb = (int)std::min<long long>((P.k + 255) / 256, 4096);
+        hipLaunchKernelGGL(frm_mark_starts_kernel, dim3(mb), dim3(256), 0, s, O.starts, P.k, P.N1, marks);
+        DDM_CHECK_LAUNCH();
+        rc = compact_run(marks, st.match_s, P.N1, P.N1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo),
+                         st.u, st.qrows[0], st.score, P.k, st.counts, s);
+        if (rc) return rc;
+        hipLaunchKernelGGL(frm_seeds_from_starts_kernel, dim3(mb), dim3(256), 0, s, st, P.k);
+        DDM_CHECK_LAUNCH();
+    }
 
     if (P.k > 0) {
         FrmArgs fa{};
@@ -508,7 +545,8 @@ int frm_run(const FrmPlan &P, const void *D1, const void *D2, int32_t *out_i, in
     }
     const int col_blocks = (int)std::min<long long>((std::max(P.k, 1) + 255) / 256, 4096);
     hipLaunchKernelGGL(frm_collect_kernel, dim3(col_blocks, P.B), dim3(256), 0, s, st, P.k, seed_state,
-                       (const int32_t *)st.counts, query_counts, P.nhalf);
+                       (const int32_t *)st.counts, query_counts, P.nhalf, P.W1, O.pixel_tol,
+                       P.explicit_starts ? 1 : 0);
     DDM_CHECK_LAUNCH();
     return compact_run(st.match_j, st.match_s, P.N1, P.N1, P.B, P.nblk, (int32_t *)(w + P.o_bc),
                        (int32_t *)(w + P.o_bo), out_i, out_j, out_score, capacity, out_count, s,
@@ -574,7 +612,7 @@ bool cooperative_ok(int dev) {
 // only on the call's arguments, so it is captured once into a HIP graph on a
 // private capture stream, instantiated, cached (a few entries, most recently
 // used first) and replayed on the caller's stream with a single launch.
-using GraphKey = std::array<uint64_t, 24>;
+using GraphKey = std::array<uint64_t, 28>;
 
 struct GraphCache {
     std::mutex mu;
@@ -718,11 +756,15 @@ size_t ddm_frm_workspace_bytes(int B, int H1, int W1, int H2, int W2, int d, int
 }
 
 static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
-                     int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score,
-                     int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
-                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                     int grid_stride, int max_iter, const FrmOpts &O, int32_t *out_i, int32_t *out_j,
+                     float *out_score, int32_t capacity, int32_t *out_count, int32_t *seed_state,
+                     int32_t *query_counts, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     FrmPlan P;
-    int rc = frm_plan(B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P);
+    if (O.starts && O.n_starts < 0) return DDM_ERR_INVALID;
+    if (!O.starts && O.n_starts != 0) return DDM_ERR_INVALID;
+    if (!(O.pixel_tol >= 0.0) || !std::isfinite(O.pixel_tol)) return DDM_ERR_INVALID;
+    if (O.pixel_tol > 0.0 && !O.starts) return DDM_ERR_INVALID;       // the routine has no grid form of it
+    int rc = frm_plan(B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P, O.starts ? O.n_starts : -1);
     if (rc) return rc;
     if (!map_ok(D1, P.f) || !map_ok(D2, P.f)) return DDM_ERR_INVALID;
     if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
@@ -731,17 +773,20 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
     if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DDM_ERR_HIP;
-    GraphKey key = {(uint64_t)dev, (uint64_t)B, (uint64_t)(uintptr_t)D1, (uint64_t)H1, (uint64_t)W1,
+    uint64_t tol_bits;
+    std::memcpy(&tol_bits, &O.pixel_tol, sizeof(tol_bits));
+    const int h_loop = (frm_mode() == DDM_FRM_LOOP && cooperative_ok(dev)) ? 0 : P.nhalf;
+    const GraphKey key = {(uint64_t)dev, (uint64_t)B, (uint64_t)(uintptr_t)D1, (uint64_t)H1, (uint64_t)W1,
                           (uint64_t)(uintptr_t)D2, (uint64_t)H2, (uint64_t)W2, (uint64_t)d, (uint64_t)dtype,
                           (uint64_t)grid_stride, (uint64_t)max_iter, (uint64_t)(uintptr_t)out_i,
                           (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)seed_state,
-                          (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, 0, 0, 0, 0};
-    const int h_loop = (frm_mode() == DDM_FRM_LOOP && cooperative_ok(dev)) ? 0 : P.nhalf;
-    key[20] = (uint64_t)h_loop;
+                          (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, (uint64_t)h_loop,
+                          (uint64_t)(uintptr_t)O.starts, (uint64_t)(uint32_t)O.n_starts, tol_bits,
+                          (uint64_t)(uintptr_t)O.basin};
     return run_graphed(key, stream, [&](hipStream_t s) {
-        return frm_run(P, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts, workspace,
-                       s, h_loop);
+        return frm_run(P, O, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts,
+                       workspace, s, h_loop);
     });
 }
 
@@ -749,16 +794,36 @@ int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2
                   int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
                   int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *workspace,
                   size_t workspace_bytes, hipStream_t stream) {
-    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, out_i, out_j, out_score, capacity,
-                     out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
+    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, FrmOpts{}, out_i, out_j, out_score,
+                     capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
 }
 
 int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
                           int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score,
                           int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return frm_entry(B, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, out_i, out_j, out_score, capacity,
-                     out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
+    return frm_entry(B, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, FrmOpts{}, out_i, out_j, out_score,
+                     capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
+}
+
+size_t ddm_frm_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int grid_stride, int n_starts,
+                                  int max_iter) {
+    FrmPlan P;
+    return frm_plan(1, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P, n_starts < 0 ? -1 : n_starts) == DDM_OK
+               ? P.total
+               : 0;
+}
+
+int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                     int grid_stride, const int32_t *starts, int n_starts, int max_iter, double pixel_tol,
+                     int32_t *basin, int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
+                     int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    FrmOpts O;
+    O.starts = starts; O.n_starts = starts ? n_starts : 0; O.pixel_tol = pixel_tol; O.basin = basin;
+    if (!starts && n_starts > 0) return DDM_ERR_INVALID;
+    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, O, out_i, out_j, out_score,
+                     capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
 }
 
 size_t ddm_mutual_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype) {

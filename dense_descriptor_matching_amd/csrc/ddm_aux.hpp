@@ -226,28 +226,58 @@ struct FrmState {
     int32_t *act[2], *qrows[2];
     int32_t *counts;
     int32_t *match_j; float *match_s;
+    int32_t *uprev, *uiter;   // u before the seed's last backward step, and that step's iteration (-1 none)
+    int32_t *basin;           // [pair][N1] or null: basin variant (forward test off, record every backward step)
     long long k_bs;        // elements between pairs for the k-sized arrays
     long long cnt_bs;      // elements between pairs for counts
     long long n1_bs;       // elements between pairs for match arrays
 };
 
-// Seed grid (rows S/2 + S*n < H1, columns S/2 + S*n < W1, p = x + W1*y,
-// ascending) and the initial state; also clears the dense match array.
+__device__ __forceinline__ void frm_seed_reset(const FrmState &st, long long ka, int a, int p) {
+    st.u[ka] = p; st.v[ka] = -1; st.conv[ka] = -1; st.score[ka] = 0.f;
+    st.act[0][ka] = a; st.qrows[0][ka] = p;
+    st.uprev[ka] = p; st.uiter[ka] = -1;
+}
+
+// Initial state. Grid seeds (k > 0 of them: rows S/2 + S*n < H1, columns
+// S/2 + S*n < W1, p = x + W1*y, ascending) are written here; with explicit
+// starts (marks != null) the seeds come later from the start marks and the
+// kernel only clears the marks. Also clears the dense match array, the basin
+// map and the control words of the loop kernel (barrier arrivals, error flag).
 __global__ void __launch_bounds__(256) frm_init_kernel(FrmState st, int k, int kx, int W1, int S, int N1,
-                                                       int nhalf, uint32_t *ctl) {
-    // control words of the single-launch loop: barrier arrivals and error flag
+                                                       int nhalf, uint32_t *ctl, int32_t *marks) {
     if (ctl && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) ctl[threadIdx.x * 32] = 0;
     const int pair = blockIdx.y;
     const long long ko = pair * st.k_bs;
-    for (int a = blockIdx.x * 256 + threadIdx.x; a < k; a += gridDim.x * 256) {
-        const int y = S / 2 + (a / kx) * S, x = S / 2 + (a % kx) * S;
-        const int p = x + W1 * y;
-        st.u[ko + a] = p; st.v[ko + a] = -1; st.conv[ko + a] = -1; st.score[ko + a] = 0.f;
-        st.act[0][ko + a] = a; st.qrows[0][ko + a] = p;
+    if (!marks)
+        for (int a = blockIdx.x * 256 + threadIdx.x; a < k; a += gridDim.x * 256) {
+            const int y = S / 2 + (a / kx) * S, x = S / 2 + (a % kx) * S;
+            frm_seed_reset(st, ko + a, a, x + W1 * y);
+        }
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < N1; i += gridDim.x * 256) {
+        st.match_j[pair * st.n1_bs + i] = -1;
+        if (marks) marks[pair * st.n1_bs + i] = -1;
+        if (st.basin) st.basin[pair * st.n1_bs + i] = -1;
     }
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < N1; i += gridDim.x * 256) st.match_j[pair * st.n1_bs + i] = -1;
     if (blockIdx.x == 0)
         for (int h = threadIdx.x; h <= nhalf; h += 256) st.counts[pair * st.cnt_bs + h] = (h == 0) ? k : 0;
+}
+
+// Explicit starts: mark every start inside image 1 (marks[p] = p); entries
+// outside [0, N1) are ignored. An ordered compaction of the marks then lists
+// the distinct starts in ascending order with their count.
+__global__ void __launch_bounds__(256) frm_mark_starts_kernel(const int32_t *starts, int n, int N1, int32_t *marks) {
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < n; e += gridDim.x * 256) {
+        const int p = starts[e];
+        if (p >= 0 && p < N1) marks[p] = p;
+    }
+}
+
+// Seeds from the compacted starts (u[a] and qrows[0][a] already hold them).
+__global__ void __launch_bounds__(256) frm_seeds_from_starts_kernel(FrmState st, int kcap) {
+    const int k = st.counts[0];
+    for (int a = blockIdx.x * 256 + threadIdx.x; a < kcap && a < k; a += gridDim.x * 256)
+        frm_seed_reset(st, a, a, st.u[a]);
 }
 
 // One half-step's update for query block blk of pair `pair`: resolve each
@@ -274,12 +304,16 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
             if (valid && sub == 0) {
                 seed = st.act[cur][ko + x];
                 if (!backward) {
-                    keep = (j != st.v[ko + seed]);
+                    keep = st.basin != nullptr || j != st.v[ko + seed];    // no forward test in the basin variant
                     st.v[ko + seed] = j;
                     st.score[ko + seed] = s;
                 } else {
-                    keep = (j != st.u[ko + seed]);
+                    const int from = st.u[ko + seed];
+                    keep = (j != from);
                     st.u[ko + seed] = j;
+                    st.uprev[ko + seed] = from;
+                    st.uiter[ko + seed] = iter;
+                    if (st.basin) st.basin[pair * st.n1_bs + from] = j;
                 }
                 if (!keep) st.conv[ko + seed] = iter;
             }
@@ -300,20 +334,49 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
 
 // Converged seeds -> dense match array indexed by image-1 pixel (every seed
 // that reaches pixel u reports the same v and score), optional seed states.
-__global__ void __launch_bounds__(256) frm_collect_kernel(FrmState st, int k, int32_t *seed_state,
+// Kept seeds -> dense match array indexed by the reported image-1 pixel
+// (every seed reporting pixel i reports the same j and score), optional seed
+// states (u, v, iteration of convergence or -1, u_old; -1 rows past the seed
+// count). u_old = u at the start of the last iteration when the loop ran
+// iteration max_iter, else the final u. pixel_tol == 0: kept = not active,
+// reported pixel u. pixel_tol > 0: kept = pixel distance |yx(u_old) - yx(u)|
+// below pixel_tol (in double, as a Euclidean distance), reported pixel u_old
+// when report_old (explicit starts), else u.
+__global__ void __launch_bounds__(256) frm_collect_kernel(FrmState st, int kcap, int32_t *seed_state,
                                                           const int32_t *counts_in, int32_t *query_counts,
-                                                          int nhalf) {
+                                                          int nhalf, int W1, double pixel_tol, int report_old) {
     const int pair = blockIdx.y;
     const long long ko = pair * st.k_bs;
-    for (int a = blockIdx.x * 256 + threadIdx.x; a < k; a += gridDim.x * 256) {
+    const int32_t *cnt = counts_in + pair * st.cnt_bs;
+    const int k = cnt[0];
+    const bool ran_last = cnt[nhalf - 2] > 0;      // forward queries of the last iteration
+    const int max_iter = nhalf / 2;
+    for (int a = blockIdx.x * 256 + threadIdx.x; a < kcap; a += gridDim.x * 256) {
+        if (a >= k) {
+            if (seed_state) {
+                int32_t *ss = seed_state + (pair * (long long)kcap + a) * 4;
+                ss[0] = -1; ss[1] = -1; ss[2] = -1; ss[3] = -1;
+            }
+            continue;
+        }
         const int u = st.u[ko + a], v = st.v[ko + a], it = st.conv[ko + a];
-        if (it >= 0) {
-            st.match_j[pair * st.n1_bs + u] = v;
-            st.match_s[pair * st.n1_bs + u] = st.score[ko + a];
+        const int uold = (ran_last && st.uiter[ko + a] == max_iter) ? st.uprev[ko + a] : u;
+        bool kept;
+        int i = u;
+        if (pixel_tol > 0.0) {
+            const double dy = (double)(uold / W1 - u / W1), dx = (double)(uold % W1 - u % W1);
+            kept = sqrt(dy * dy + dx * dx) < pixel_tol;
+            if (report_old) i = uold;
+        } else {
+            kept = it >= 0;
+        }
+        if (kept) {
+            st.match_j[pair * st.n1_bs + i] = v;
+            st.match_s[pair * st.n1_bs + i] = st.score[ko + a];
         }
         if (seed_state) {
-            int32_t *ss = seed_state + (pair * (long long)k + a) * 4;
-            ss[0] = u; ss[1] = v; ss[2] = it; ss[3] = 0;
+            int32_t *ss = seed_state + (pair * (long long)kcap + a) * 4;
+            ss[0] = u; ss[1] = v; ss[2] = it; ss[3] = uold;
         }
     }
     if (query_counts && blockIdx.x == 0)

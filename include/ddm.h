@@ -94,7 +94,7 @@ int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, i
  *   out_count                device int32: number of pairs written
  *   seed_state               device int32[k][4] or NULL: per seed (in grid
  *                            order) u, v, iteration in which it converged
- *                            (-1 if it did not), 0
+ *                            (-1 if it did not), u_old (see ddm_frm_match_ex)
  *   query_counts             device int32[2*max_iter] or NULL: number of
  *                            forward / backward NN queries in each iteration
  *                            (entry 2t = forward, 2t+1 = backward of iteration t+1)
@@ -120,6 +120,35 @@ int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2,
                           int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
                           int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* FRM with the routine's other options ("DUSt3R和MASt3R论文阅读", section MASt3R matching, the quoted
+ * fast_reciprocal_NNs routine; one pair):
+ *   starts      NULL: seeds on the stride-`grid_stride` grid as in ddm_frm_match.
+ *               Else device int32[n_starts] linear image-1 pixels (p = x + W1*y); entries outside
+ *               [0, H1*W1) are ignored, the rest are made unique and ascending (k = their number).
+ *               The routine runs one iteration for such starts; max_iter is still the caller's.
+ *   pixel_tol   0: a seed's pair is kept when the seed is no longer active at the end (as in
+ *               ddm_frm_match). > 0 (explicit starts only, else DDM_ERR_INVALID): a seed is kept
+ *               when the Euclidean distance in pixels between u_old and u is below pixel_tol, and
+ *               its pair is reported at u_old, where u_old is the seed's image-1 pixel at the start
+ *               of the last iteration if the loop ran all max_iter iterations, else its final pixel
+ *               (with max_iter = 1: the start itself).
+ *   basin       NULL, or device int32[H1*W1]: the basin variant. The forward test is off (a seed
+ *               stops only when its backward query returns the pixel it started the iteration
+ *               from) and every backward query of a seed standing at pixel p stores the pixel it
+ *               moved to at basin[p]; pixels never left by a backward query hold -1.
+ *   capacity    >= k (ddm_seed_count for the grid, n_starts for explicit starts).
+ *   seed_state  as for ddm_frm_match, with entry 3 = u_old; rows past the number of distinct
+ *               starts are -1.
+ * The workspace size comes from ddm_frm_ex_workspace_bytes with n_starts = -1 for the grid. */
+size_t ddm_frm_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int grid_stride,
+                                  int n_starts, int max_iter);
+int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                     int grid_stride, const int32_t *starts, int n_starts, int max_iter, double pixel_tol,
+                     int32_t *basin,
+                     int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
+                     int32_t *seed_state, int32_t *query_counts,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* How FRM calls are executed (process-wide; results are identical):
  *   DDM_FRM_PER_HALF_STEP (default): a sweep and an update launch for every

@@ -99,6 +99,37 @@ def test_frm_rejects_bad_arguments(L):
     assert _frm(L, D2=FAKE + 2, dtype=0) == -1          # fp32 map not 4-byte aligned
 
 
+def _frm_ex(L, **kw):
+    a = dict(D1=FAKE, H1=64, W1=48, D2=FAKE, H2=64, W2=48, d=24, dtype=1, S=8, starts=FAKE, n=100, it=1,
+             tol=0.0, basin=None, oi=FAKE, oj=FAKE, os=FAKE, cap=100, cnt=FAKE, st=None, qc=None, ws=FAKE,
+             wsb=1 << 40)
+    a.update(kw)
+    return L.ddm_frm_match_ex(a["D1"], a["H1"], a["W1"], a["D2"], a["H2"], a["W2"], a["d"], a["dtype"], a["S"],
+                              a["starts"], a["n"], a["it"], a["tol"], a["basin"], a["oi"], a["oj"], a["os"],
+                              a["cap"], a["cnt"], a["st"], a["qc"], a["ws"], a["wsb"], None)
+
+
+def test_frm_ex_rejects_bad_arguments(L):
+    import math
+    assert _frm_ex(L, starts=None, n=5) == -1              # a count without a list
+    assert _frm_ex(L, n=-1) == -1
+    assert _frm_ex(L, tol=-0.5) == -1
+    assert _frm_ex(L, tol=math.nan) == -1
+    assert _frm_ex(L, tol=math.inf) == -1
+    assert _frm_ex(L, starts=None, n=0, tol=1.0) == -1     # pixel_tol needs explicit starts
+    assert _frm_ex(L, cap=99) == -2                        # capacity below the number of starts
+    assert _frm_ex(L, starts=None, n=0, cap=47) == -2      # grid: 48 seeds
+    assert _frm_ex(L, it=0) == -1
+    assert _frm_ex(L, wsb=16) == -3
+    assert _frm_ex(L, D1=FAKE + 2) == -1
+    # workspace: explicit starts need room for their marks and states; invalid requests report 0
+    g = L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 8, -1, 10)
+    assert g == L.ddm_frm_workspace_bytes(1, 64, 48, 64, 48, 24, 1, 8, 10) > 0
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 8, 5000, 1) > g
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, -1, 10) == 0
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, 10, 1) > 0     # stride unused with starts
+
+
 def test_frm_batched_rejects_bad_batch(L):
     r = L.ddm_frm_match_batched(0, FAKE, 64, 48, FAKE, 64, 48, 24, 1, 8, 10, FAKE, FAKE, FAKE, 48, FAKE, None,
                                 None, FAKE, 1 << 40, None)
