@@ -22,6 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, F16, BF16 = 0, 1, 2
+METRICS = {"dot": 0, "l2": 1}     # score = dot product, or minus the squared Euclidean distance
 
 
 def build(force: bool = True) -> str:
@@ -48,7 +49,11 @@ def _bind(path: str):
     lib.orc_seed_grid.restype = i64
     lib.orc_frm.argtypes = [P, i64, P, i64, i32, P, i64, i32, dbl, P, P, P, P, P, P, P, P]
     lib.orc_frm.restype = i32
-    lib.orc_frm_ex.argtypes = [P, i64, P, i64, i32, P, i64, i32, dbl, i32, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_frm_ex.argtypes = [P, i64, P, i64, i32, i32, P, i64, i32, dbl, i32, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_nn_m.argtypes = [P, P, i64, P, i64, i32, i32, P, P, P]
+    lib.orc_nn_m.restype = None
+    lib.orc_mutual_m.argtypes = [P, i64, P, i64, i32, i32, P, P, P, P, P, P, P, P, P]
+    lib.orc_mutual_m.restype = i64
     lib.orc_frm_ex.restype = i32
     lib.orc_frm_select.argtypes = [P, P, P, i64, i32, dbl, i32, P, P]
     lib.orc_frm_select.restype = None
@@ -109,10 +114,11 @@ def _rows(x: np.ndarray) -> np.ndarray:
     return x.reshape(-1, x.shape[-1])
 
 
-def nn(Q: np.ndarray, R: np.ndarray, qrows=None):
+def nn(Q: np.ndarray, R: np.ndarray, qrows=None, metric: str = "dot"):
     """Brute-force NN of rows of Q (or of Q[qrows]) over all rows of R.
 
-    Returns (idx int32, s1 float64, margin float64)."""
+    metric "dot": score = dot product; "l2": score = minus the squared Euclidean
+    distance (the NN is the nearest point). Returns (idx int32, s1 float64, margin float64)."""
     lib = _load()
     Q, R = _rows(Q), _rows(R)
     d = Q.shape[1]
@@ -124,8 +130,8 @@ def nn(Q: np.ndarray, R: np.ndarray, qrows=None):
     idx = np.empty(nq, np.int32)
     s1 = np.empty(nq, np.float64)
     s2 = np.empty(nq, np.float64)
-    lib.orc_nn(_p(Q), _p(qrows) if qrows is not None else None, nq, _p(R), R.shape[0], d,
-               _p(idx), _p(s1), _p(s2))
+    lib.orc_nn_m(_p(Q), _p(qrows) if qrows is not None else None, nq, _p(R), R.shape[0], d, METRICS[metric],
+                 _p(idx), _p(s1), _p(s2))
     return idx, s1, s1 - s2
 
 
@@ -163,7 +169,7 @@ def frm(D1: np.ndarray, D2: np.ndarray, seeds: np.ndarray, max_iter: int, tau: f
 
 def frm_ex(D1: np.ndarray, D2: np.ndarray, H1: int, W1: int, *, grid_stride: int | None = None,
            starts: np.ndarray | None = None, max_iter: int = 10, pixel_tol: float = 0.0, ret_basin: bool = False,
-           tau: float = 1e-4):
+           tau: float = 1e-4, metric: str = "dot"):
     """The FRM routine with its options ("DUSt3R和MASt3R论文阅读", section MASt3R matching, the quoted
     fast_reciprocal_NNs routine):
 
@@ -174,7 +180,9 @@ def frm_ex(D1: np.ndarray, D2: np.ndarray, H1: int, W1: int, *, grid_stride: int
       the Euclidean pixel distance between u_old, as the loop leaves it, and u is below pixel_tol; the
       reported image-1 pixel is u_old (the start itself in a one-iteration call);
     - ``ret_basin``: the forward test is off and basin[p] (N1 entries, -1 elsewhere) records, for each
-      backward query, where a seed that stood at p moved to.
+      backward query, where a seed that stood at p moved to;
+    - ``metric``: "dot" (descriptors) or "l2" (3D points: nearest by Euclidean distance; scores are
+      then minus squared distances).
 
     Returns a dict with the per-seed state (seeds, u, v, u_old, score, conv_iter, active, ambiguous),
     the unique pairs i, j, s ascending in (i, j), basin (or None), niter, n_fwd, n_bwd."""
@@ -200,7 +208,7 @@ def frm_ex(D1: np.ndarray, D2: np.ndarray, H1: int, W1: int, *, grid_stride: int
     active = np.empty(k, np.uint8); amb = np.empty(k, np.uint8)
     nf = np.zeros(max(max_iter, 1), np.int64); nb = np.zeros(max(max_iter, 1), np.int64)
     basin = np.full(N1, -1, np.int32) if ret_basin else None
-    niter = lib.orc_frm_ex(_p(A), N1, _p(B), B.shape[0], A.shape[1], _p(seeds), k, max_iter, tau,
+    niter = lib.orc_frm_ex(_p(A), N1, _p(B), B.shape[0], A.shape[1], METRICS[metric], _p(seeds), k, max_iter, tau,
                            0 if ret_basin else 1, _p(basin) if ret_basin else None, _p(u_old),
                            _p(u), _p(v), _p(score), _p(conv), _p(active), _p(amb), _p(nf), _p(nb))
     if niter < 0:
@@ -220,16 +228,17 @@ def frm_ex(D1: np.ndarray, D2: np.ndarray, H1: int, W1: int, *, grid_stride: int
                 basin=basin, niter=int(niter), n_fwd=nf[:max_iter], n_bwd=nb[:max_iter])
 
 
-def mutual(D1: np.ndarray, D2: np.ndarray):
-    """Exhaustive mutual NN. Returns dict with pairs i, j, s and both NN tables with margins."""
+def mutual(D1: np.ndarray, D2: np.ndarray, metric: str = "dot"):
+    """Exhaustive mutual NN. Returns dict with pairs i, j, s and both NN tables with margins
+    (metric as in :func:`nn`)."""
     lib = _load()
     A, B = _rows(D1), _rows(D2)
     N1, N2, d = A.shape[0], B.shape[0], A.shape[1]
     nn12 = np.empty(N1, np.int32); s12 = np.empty(N1); m12 = np.empty(N1)
     nn21 = np.empty(N2, np.int32); s21 = np.empty(N2); m21 = np.empty(N2)
     oi = np.empty(min(N1, N2), np.int32); oj = np.empty(min(N1, N2), np.int32); os_ = np.empty(min(N1, N2))
-    n = lib.orc_mutual(_p(A), N1, _p(B), N2, d, _p(nn12), _p(s12), _p(m12), _p(nn21), _p(s21), _p(m21),
-                       _p(oi), _p(oj), _p(os_))
+    n = lib.orc_mutual_m(_p(A), N1, _p(B), N2, d, METRICS[metric], _p(nn12), _p(s12), _p(m12),
+                         _p(nn21), _p(s21), _p(m21), _p(oi), _p(oj), _p(os_))
     if n < 0:
         raise MemoryError
     return dict(i=oi[:n].copy(), j=oj[:n].copy(), s=os_[:n].copy(), nn12=nn12, s12=s12, m12=m12,

@@ -87,32 +87,61 @@ static double dot(const double *a, const double *b, int d)
     return s;
 }
 
+/* Score of the Euclidean metric: minus the squared distance, in double, c
+ * ascending, so that the nearest point is the one of maximum score. The pages
+ * match 3D points (d = 3) by this distance ("DUSt3R和MASt3R论文阅读", section
+ * MASt3R matching: K-d trees for x in R^3). */
+static double neg_sqdist(const double *a, const double *b, int d)
+{
+    double s = 0.0;
+    for (int c = 0; c < d; ++c) {
+        const double t = a[c] - b[c];
+        s -= t * t;
+    }
+    return s;
+}
+
+enum { ORC_DOT = 0, ORC_L2 = 1 };
+
 /* Brute-force NN of one query over all n rows of R: the smallest index that
  * attains the maximum score, the maximum s1 and the best score s2 over every
- * other index (s2 == s1 when the maximum is attained twice). */
-static void nn_one(const double *q, const double *R, int64_t n, int d,
-                   int32_t *idx, double *s1, double *s2)
+ * other index (s2 == s1 when the maximum is attained twice). The score is the
+ * dot product (ORC_DOT) or minus the squared Euclidean distance (ORC_L2). */
+static void nn_one_m(const double *q, const double *R, int64_t n, int d, int metric,
+                     int32_t *idx, double *s1, double *s2)
 {
     int32_t best = -1;
     double b1 = -INFINITY, b2 = -INFINITY;
     for (int64_t j = 0; j < n; ++j) {
-        double s = dot(q, R + j * d, d);
+        double s = metric == ORC_L2 ? neg_sqdist(q, R + j * d, d) : dot(q, R + j * d, d);
         if (s > b1) { b2 = b1; b1 = s; best = (int32_t)j; }
         else if (s > b2) { b2 = s; }
     }
     *idx = best; *s1 = b1; *s2 = b2;
 }
 
+static void nn_one(const double *q, const double *R, int64_t n, int d, int32_t *idx, double *s1, double *s2)
+{
+    nn_one_m(q, R, n, d, ORC_DOT, idx, s1, s2);
+}
+
 /* NN for a list of queries: row qrows[a] of Q (or row a when qrows is NULL). */
-void orc_nn(const double *Q, const int32_t *qrows, int64_t nq,
-            const double *R, int64_t nr, int d,
-            int32_t *idx, double *s1, double *s2)
+void orc_nn_m(const double *Q, const int32_t *qrows, int64_t nq,
+              const double *R, int64_t nr, int d, int metric,
+              int32_t *idx, double *s1, double *s2)
 {
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t a = 0; a < nq; ++a) {
         int64_t r = qrows ? qrows[a] : a;
-        nn_one(Q + r * d, R, nr, d, &idx[a], &s1[a], &s2[a]);
+        nn_one_m(Q + r * d, R, nr, d, metric, &idx[a], &s1[a], &s2[a]);
     }
+}
+
+void orc_nn(const double *Q, const int32_t *qrows, int64_t nq,
+            const double *R, int64_t nr, int d,
+            int32_t *idx, double *s1, double *s2)
+{
+    orc_nn_m(Q, qrows, nq, R, nr, d, ORC_DOT, idx, s1, s2);
 }
 
 /* Seed grid [FRM-listing]: rows y = S/2, S/2 + S, ... < H and columns
@@ -165,7 +194,7 @@ int64_t orc_seed_grid(int H, int W, int S, int32_t *out)
  *                 loop stopped at max_iter, the final u if it stopped because
  *                 no seed was active (the copy is refreshed after every
  *                 iteration that does not hit max_iter). */
-int orc_frm_ex(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
+int orc_frm_ex(const double *D1, int64_t N1, const double *D2, int64_t N2, int d, int metric,
                const int32_t *seeds, int64_t k, int max_iter, double tau, int fwd_test,
                int32_t *basin, int32_t *u_old_out,
                int32_t *u, int32_t *v, double *score, int32_t *conv_iter,
@@ -195,7 +224,7 @@ int orc_frm_ex(const double *D1, int64_t N1, const double *D2, int64_t N2, int d
         for (int64_t a = 0; a < k; ++a) {
             if (!active[a]) continue;
             int32_t j; double s1, s2;
-            nn_one(D1 + (int64_t)u[a] * d, D2, N2, d, &j, &s1, &s2);
+            nn_one_m(D1 + (int64_t)u[a] * d, D2, N2, d, metric, &j, &s1, &s2);
             v[a] = j; score[a] = s1;
             if (s1 - s2 < tau) ambiguous[a] = 1;
         }
@@ -209,7 +238,7 @@ int orc_frm_ex(const double *D1, int64_t N1, const double *D2, int64_t N2, int d
         for (int64_t a = 0; a < k; ++a) {
             if (!active[a]) continue;
             int32_t i; double s1, s2;
-            nn_one(D2 + (int64_t)v[a] * d, D1, N1, d, &i, &s1, &s2);
+            nn_one_m(D2 + (int64_t)v[a] * d, D1, N1, d, metric, &i, &s1, &s2);
             u[a] = i;
             if (s1 - s2 < tau) ambiguous[a] = 1;
         }
@@ -235,8 +264,8 @@ int orc_frm(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
             int32_t *u, int32_t *v, double *score, int32_t *conv_iter,
             uint8_t *active, uint8_t *ambiguous, int64_t *n_fwd, int64_t *n_bwd)
 {
-    return orc_frm_ex(D1, N1, D2, N2, d, seeds, k, max_iter, tau, 1, NULL, NULL, u, v, score, conv_iter, active,
-                      ambiguous, n_fwd, n_bwd);
+    return orc_frm_ex(D1, N1, D2, N2, d, ORC_DOT, seeds, k, max_iter, tau, 1, NULL, NULL, u, v, score, conv_iter,
+                      active, ambiguous, n_fwd, n_bwd);
 }
 
 /* Which seeds the routine keeps, and the image-1 pixel it reports for each
@@ -301,16 +330,16 @@ int64_t orc_merge(const int32_t *u, const int32_t *v, const double *score, const
  * M = {(i, j) : j = NN2(D1_i) and i = NN1(D2_j)}, ascending in i.
  * nn12 / s12 / m12 (size N1) and nn21 / s21 / m21 (size N2) receive both NN
  * tables with scores and margins. Returns |M|. */
-int64_t orc_mutual(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
-                   int32_t *nn12, double *s12, double *m12,
-                   int32_t *nn21, double *s21, double *m21,
-                   int32_t *out_i, int32_t *out_j, double *out_s)
+int64_t orc_mutual_m(const double *D1, int64_t N1, const double *D2, int64_t N2, int d, int metric,
+                     int32_t *nn12, double *s12, double *m12,
+                     int32_t *nn21, double *s21, double *m21,
+                     int32_t *out_i, int32_t *out_j, double *out_s)
 {
     double *t1 = (double *)malloc(sizeof(double) * (size_t)(N1 > N2 ? N1 : N2));
     if (!t1) return -1;
-    orc_nn(D1, NULL, N1, D2, N2, d, nn12, s12, t1);
+    orc_nn_m(D1, NULL, N1, D2, N2, d, metric, nn12, s12, t1);
     for (int64_t i = 0; i < N1; ++i) m12[i] = s12[i] - t1[i];
-    orc_nn(D2, NULL, N2, D1, N1, d, nn21, s21, t1);
+    orc_nn_m(D2, NULL, N2, D1, N1, d, metric, nn21, s21, t1);
     for (int64_t j = 0; j < N2; ++j) m21[j] = s21[j] - t1[j];
     free(t1);
     int64_t n = 0;
@@ -322,4 +351,12 @@ int64_t orc_mutual(const double *D1, int64_t N1, const double *D2, int64_t N2, i
         }
     }
     return n;
+}
+
+int64_t orc_mutual(const double *D1, int64_t N1, const double *D2, int64_t N2, int d,
+                   int32_t *nn12, double *s12, double *m12,
+                   int32_t *nn21, double *s21, double *m21,
+                   int32_t *out_i, int32_t *out_j, double *out_s)
+{
+    return orc_mutual_m(D1, N1, D2, N2, d, ORC_DOT, nn12, s12, m12, nn21, s21, m21, out_i, out_j, out_s);
 }

@@ -194,3 +194,40 @@ def gaussian_rows(n: int, d: int, dtype: int, seed: int, unit: bool = True) -> n
     rng = np.random.Generator(np.random.PCG64(seed))
     x = rng.standard_normal((n, d))
     return cast_stored(_unit(x) if unit else x, dtype)
+
+
+# ---------------------------------------------------------------------------
+# Pointmaps (3D points per pixel), for nearest-neighbour search by Euclidean
+# distance: the pages match 3D points with K-d trees ("DUSt3R和MASt3R论文阅读",
+# section MASt3R matching, d = 3). A pointmap gives, per pixel, the 3D point
+# seen along its ray (same blog, DUSt3R section on PointMap).
+# ---------------------------------------------------------------------------
+def _surface_points(xs: np.ndarray, ys: np.ndarray, H: int, W: int, waves: np.ndarray) -> np.ndarray:
+    """Points of a smooth random depth surface seen by a pinhole camera: depth
+    z(x, y) = 2 + sum_k a_k sin(f_k . (x, y) / W + phi_k), point = (z (x - W/2) / W,
+    z (y - H/2) / W, z). Defined for any real pixel coordinates."""
+    z = 2.0 + np.zeros_like(xs, dtype=np.float64)
+    for a, fx, fy, ph in waves:
+        z += a * np.sin((fx * xs + fy * ys) / W + ph)
+    return np.stack([z * (xs - W / 2) / W, z * (ys - H / 2) / W, z], axis=-1)
+
+
+def pointmap_pair(H: int, W: int, seed: int, *, shift=(0, 0), sigma: float = 0.0,
+                  H2: int | None = None, W2: int | None = None):
+    """Two float32 pointmaps [H, W, 3] of one surface in one world frame:
+    P1(x, y) = surface(x, y); P2(x, y) = surface(x + dx, y + dy) + sigma * N(0, 1) per
+    coordinate (noise drawn after the surface). With sigma == 0 and an integer shift,
+    the in-range pixels of P2 hold exactly the float32 points of P1 at the source."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    waves = np.stack([rng.uniform(0.05, 0.3, 6), rng.uniform(-12, 12, 6), rng.uniform(-12, 12, 6),
+                      rng.uniform(0, 2 * math.pi, 6)], axis=1)
+    H2 = H if H2 is None else H2
+    W2 = W if W2 is None else W2
+    ys, xs = np.mgrid[0:H, 0:W].astype(np.float64)
+    P1 = _surface_points(xs, ys, H, W, waves).astype(np.float32)
+    ys2, xs2 = np.mgrid[0:H2, 0:W2].astype(np.float64)
+    P2 = _surface_points(xs2 + shift[0], ys2 + shift[1], H, W, waves)
+    noise = rng.standard_normal(P2.shape)
+    if sigma > 0:
+        P2 = P2 + sigma * noise
+    return P1, P2.astype(np.float32)

@@ -36,10 +36,14 @@ MUTATIONS = {
     "max_iter_off_by_one": ("if (niter >= max_iter) break;", "if (niter > max_iter) break;"),
     "old_not_updated": ("for (int64_t a = 0; a < k; ++a) { v_old[a] = v[a]; u_old[a] = u[a]; }",
                         "for (int64_t a = 0; a < k; ++a) { v_old[a] = v[a]; }"),
-    "backward_against_own_map": ("nn_one(D2 + (int64_t)v[a] * d, D1, N1, d, &i, &s1, &s2);",
-                                 "nn_one(D2 + (int64_t)v[a] * d, D2, N2, d, &i, &s1, &s2);"),
-    "forward_query_from_wrong_map": ("nn_one(D1 + (int64_t)u[a] * d, D2, N2, d, &j, &s1, &s2);",
-                                     "nn_one(D2 + (int64_t)u[a] * d, D2, N2, d, &j, &s1, &s2);"),
+    "backward_against_own_map": ("nn_one_m(D2 + (int64_t)v[a] * d, D1, N1, d, metric, &i, &s1, &s2);",
+                                 "nn_one_m(D2 + (int64_t)v[a] * d, D2, N2, d, metric, &i, &s1, &s2);"),
+    "forward_query_from_wrong_map": ("nn_one_m(D1 + (int64_t)u[a] * d, D2, N2, d, metric, &j, &s1, &s2);",
+                                     "nn_one_m(D2 + (int64_t)u[a] * d, D2, N2, d, metric, &j, &s1, &s2);"),
+    "l2_unsquared": ("        s -= t * t;", "        s -= t < 0 ? -t : t;"),
+    "l2_sign_flipped": ("        s -= t * t;", "        s += t * t;"),
+    "l2_metric_ignored": ("double s = metric == ORC_L2 ? neg_sqdist(q, R + j * d, d) : dot(q, R + j * d, d);",
+                          "double s = dot(q, R + j * d, d);"),
     "converged_keeps_active": ("if (active[a]) continue;\n        buf[3 * m]", "if (!active[a]) continue;\n        buf[3 * m]"),
     "basin_at_new_pixel": ("if (active[a]) basin[u_old[a]] = u[a];", "if (active[a]) basin[u[a]] = u[a];"),
     "u_old_export_is_u": ("u_old_out[a] = u_old[a];", "u_old_out[a] = u[a];"),
@@ -75,6 +79,10 @@ PINS = [
     lambda: P.test_frm_ex_equals_orbit_derivation((12, 9), 24, 63, 2, 2.5, False),
     lambda: P.test_frm_ex_equals_orbit_derivation((1, 40), 2, 64, 10, 1.0, False),
     P.test_frm_ex_identity_and_shift_closed_forms,
+    P.test_l2_nn_matches_kdtree,
+    P.test_l2_nn_ties_and_numpy,
+    P.test_l2_mutual_matches_numpy,
+    lambda: P.test_l2_frm_equals_orbit_derivation(3),
 ]
 
 

@@ -389,6 +389,79 @@ def test_frm_ex_rejects_undefined_requests():
     assert r["i"].size == 0
 
 
+# ------------------------------------------------------------ Euclidean metric (3D points)
+def _np_nn_l2(A, B):
+    """NN by squared Euclidean distance from numpy broadcasting: argmin (first = lowest index)."""
+    A = A.reshape(-1, A.shape[-1]).astype(np.float64); B = B.reshape(-1, B.shape[-1]).astype(np.float64)
+    D = ((A[:, None, :] - B[None, :, :]) ** 2).sum(-1)
+    idx = D.argmin(1)
+    srt = np.sort(D, axis=1)
+    second = srt[:, 1] if D.shape[1] > 1 else np.full(D.shape[0], np.inf)
+    return idx, srt[:, 0], second - srt[:, 0]
+
+
+def test_l2_nn_matches_kdtree():
+    from scipy.spatial import cKDTree
+    rng = np.random.default_rng(81)
+    A = rng.standard_normal((300, 3)); B = rng.standard_normal((500, 3))
+    idx, s1, m = oracle.nn(A, B, metric="l2")
+    dist, kidx = cKDTree(B).query(A)
+    assert np.array_equal(idx, kidx)
+    np.testing.assert_allclose(-s1, dist ** 2, rtol=1e-12, atol=1e-15)
+    assert np.all(m > 0)
+
+
+def test_l2_nn_ties_and_numpy():
+    rng = np.random.default_rng(82)
+    B = rng.standard_normal((64, 3)).astype(np.float32).astype(np.float64)
+    B[40] = B[7]; B[50] = B[7]                       # exact duplicates: lowest index wins
+    A = np.concatenate([B[[7, 40, 3]], rng.standard_normal((20, 3))])
+    idx, s1, m = oracle.nn(A, B, metric="l2")
+    e_idx, e_d2, e_m = _np_nn_l2(A, B)
+    assert np.array_equal(idx, e_idx) and idx[0] == 7 and idx[1] == 7
+    np.testing.assert_allclose(-s1, e_d2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, e_m, rtol=0, atol=1e-12)
+    assert m[0] == 0.0
+
+
+def test_l2_mutual_matches_numpy():
+    P1, P2 = synth.pointmap_pair(10, 12, 83, shift=(2, -1), sigma=0.01)
+    A = P1.astype(np.float64); B = P2.astype(np.float64)
+    m = oracle.mutual(A, B, metric="l2")
+    n12 = _np_nn_l2(A, B)[0]; n21 = _np_nn_l2(B, A)[0]
+    exp = [(i, int(j)) for i, j in enumerate(n12) if n21[j] == i]
+    assert list(zip(m["i"].tolist(), m["j"].tolist())) == exp
+    assert len(exp) > 20
+
+
+@pytest.mark.parametrize("max_iter", [1, 3, 10])
+def test_l2_frm_equals_orbit_derivation(max_iter):
+    P1, P2 = synth.pointmap_pair(9, 11, 84, shift=(1, 2), sigma=0.02)
+    A = P1.astype(np.float64).reshape(-1, 3); B = P2.astype(np.float64).reshape(-1, 3)
+    seeds = np.arange(A.shape[0], dtype=np.int32)
+    r = oracle.frm_ex(A, B, 9, 11, starts=seeds, max_iter=max_iter, metric="l2")
+    nn12 = _np_nn_l2(A, B)[0]; nn21 = _np_nn_l2(B, A)[0]
+    f = nn21[nn12]
+    for a, s in enumerate(seeds):
+        x, m = int(s), 0
+        while f[x] != x and m < max_iter:
+            x, m = int(f[x]), m + 1
+        if f[x] == x and m + 1 <= max_iter:
+            assert r["conv_iter"][a] == m + 1 and r["u"][a] == x and r["v"][a] == nn12[x]
+        else:
+            assert r["conv_iter"][a] == -1
+
+
+def test_l2_pure_shift_closed_form():
+    dx, dy, H, W = 3, -2, 12, 14
+    P1, P2 = synth.pointmap_pair(H, W, 85, shift=(dx, dy))
+    A = P1.astype(np.float64); B = P2.astype(np.float64)
+    inside = [q for q in range(H * W) if 0 <= q % W - dx < W and 0 <= q // W - dy < H]
+    r = oracle.frm_ex(A, B, H, W, starts=np.array(inside), max_iter=1, metric="l2")
+    assert r["i"].tolist() == inside and r["j"].tolist() == [q - dx - dy * W for q in inside]
+    assert np.all(r["s"] == 0.0)
+
+
 # --------------------------------------------------------------------- mutual
 @pytest.mark.parametrize("s1,s2,d,seed", [((10, 12), (10, 12), 24, 51), ((7, 9), (11, 5), 3, 52),
                                           ((16, 16), (16, 16), 2, 53)])
