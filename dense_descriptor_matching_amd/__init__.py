@@ -25,6 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libddm.so")
 
 DDM_F32, DDM_F16, DDM_BF16 = 0, 1, 2
+METRICS = {"dot": 0, "l2": 1}   # dot product (descriptors) / Euclidean distance (3D points, fp32)
 _DT = {torch.float32: DDM_F32, torch.float16: DDM_F16, torch.bfloat16: DDM_BF16}
 STATUS = {0: "ok", -1: "invalid argument", -2: "output capacity too small",
           -3: "workspace missing or too small", -4: "unsupported dtype or descriptor dimension",
@@ -53,10 +54,16 @@ def _declare(lib):
     lib.ddm_mutual_workspace_bytes.argtypes = [I, I, I, I, I, I]; lib.ddm_mutual_workspace_bytes.restype = SZ
     lib.ddm_mutual_nn.argtypes = [P, I, I, P, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
     lib.ddm_mutual_nn.restype = I
-    lib.ddm_frm_ex_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
+    lib.ddm_frm_ex_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I, I]
     lib.ddm_frm_ex_workspace_bytes.restype = SZ
-    lib.ddm_frm_match_ex.argtypes = [P, I, I, P, I, I, I, I, I, P, I, I, C.c_double, P,
+    lib.ddm_frm_match_ex.argtypes = [P, I, I, P, I, I, I, I, I, I, P, I, I, C.c_double, P,
                                      P, P, P, I, P, P, P, P, SZ, P]
+    lib.ddm_nn_ex_workspace_bytes.argtypes = [I, I, I, I, I, I]; lib.ddm_nn_ex_workspace_bytes.restype = SZ
+    lib.ddm_nn_ex.argtypes = [P, I, P, I, P, I, I, I, I, P, P, P, SZ, P]; lib.ddm_nn_ex.restype = I
+    lib.ddm_mutual_ex_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.ddm_mutual_ex_workspace_bytes.restype = SZ
+    lib.ddm_mutual_nn_ex.argtypes = [P, I, I, P, I, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
+    lib.ddm_mutual_nn_ex.restype = I
     lib.ddm_frm_match_ex.restype = I
     lib.ddm_frm_set_mode.argtypes = [I]; lib.ddm_frm_set_mode.restype = I
     lib.ddm_frm_get_mode.argtypes = []; lib.ddm_frm_get_mode.restype = I
@@ -138,10 +145,11 @@ def profile_read():
 
 
 # ------------------------------------------------------------------- NN
-def nn(Q: torch.Tensor, R: torch.Tensor, q_rows: torch.Tensor | None = None):
+def nn(Q: torch.Tensor, R: torch.Tensor, q_rows: torch.Tensor | None = None, metric: str = "dot"):
     """Nearest neighbour of rows of Q (or Q[q_rows]) among all rows of R.
 
-    Q: [NQ, d] (or [..., d]), R: [N, d]. Returns (idx int32 [M], score float32 [M])."""
+    Q: [NQ, d] (or [..., d]), R: [N, d]. metric "dot" (largest dot product) or "l2" (nearest
+    point, fp32; the score is then the squared distance). Returns (idx int32 [M], score float32 [M])."""
     _check_map(Q, "Q"); _check_map(R, "R")
     d = Q.shape[-1]
     if R.shape[-1] != d or Q.dtype != R.dtype:
@@ -155,9 +163,13 @@ def nn(Q: torch.Tensor, R: torch.Tensor, q_rows: torch.Tensor | None = None):
     out_idx = torch.empty(M, dtype=torch.int32, device=Q.device)
     out_s = torch.empty(M, dtype=torch.float32, device=Q.device)
     L = lib()
-    ws = _workspace(L.ddm_nn_workspace_bytes(NQ, M, N, d, _DT[Q.dtype]), Q.device)
-    _rc(L.ddm_nn(_ptr(Q), NQ, _ptr(q_rows), M, _ptr(R), N, d, _DT[Q.dtype], _ptr(out_idx), _ptr(out_s),
-                 _ptr(ws), ws.numel(), _stream()), "ddm_nn")
+    mt = METRICS[metric]
+    nbytes = L.ddm_nn_ex_workspace_bytes(NQ, M, N, d, _DT[Q.dtype], mt)
+    if nbytes == 0:
+        raise DDMError(-4, "ddm_nn_ex_workspace_bytes (unsupported dtype, d or metric)")
+    ws = _workspace(nbytes, Q.device)
+    _rc(L.ddm_nn_ex(_ptr(Q), NQ, _ptr(q_rows), M, _ptr(R), N, d, _DT[Q.dtype], mt, _ptr(out_idx), _ptr(out_s),
+                    _ptr(ws), ws.numel(), _stream()), "ddm_nn_ex")
     return out_idx, out_s
 
 
@@ -256,7 +268,7 @@ def frm_match_batched(D1: torch.Tensor, D2: torch.Tensor, grid_stride: int = 8, 
 
 def frm_match_ex(D1: torch.Tensor, D2: torch.Tensor, *, grid_stride: int = 8, starts=None,
                  max_iter: int | None = None, pixel_tol: float = 0.0, ret_basin: bool = False,
-                 return_state: bool = False):
+                 return_state: bool = False, metric: str = "dot"):
     """FRM with the routine's options (explicit starts, pixel tolerance, basin map); one pair.
 
     ``starts``: None for the stride grid; an int tensor of linear image-1 pixels (p = x + W1*y);
@@ -265,7 +277,8 @@ def frm_match_ex(D1: torch.Tensor, D2: torch.Tensor, *, grid_stride: int = 8, st
     on the grid. ``pixel_tol > 0`` needs starts: a seed is kept when its image-1 pixel moved by
     less than pixel_tol over the last iteration, and is reported at its pixel before that
     iteration. ``ret_basin`` turns the forward test off and returns basin [H1*W1] int32
-    (where a backward query from each pixel went, -1 if none).
+    (where a backward query from each pixel went, -1 if none). ``metric`` "l2" matches fp32
+    pointmaps by Euclidean distance (scores are then squared distances).
 
     Returns (i, j, score) [+ basin] [+ dict(state=[k, 4] (u, v, conv_iter, u_old), query_counts)]."""
     _check_map(D1, "D1"); _check_map(D2, "D2")
@@ -299,11 +312,12 @@ def frm_match_ex(D1: torch.Tensor, D2: torch.Tensor, *, grid_stride: int = 8, st
     state = torch.empty(cap * 4, dtype=torch.int32, device=dev) if return_state else None
     qc = torch.zeros(2 * max_iter, dtype=torch.int32, device=dev) if return_state else None
     basin = torch.empty(H1 * W1, dtype=torch.int32, device=dev) if ret_basin else None
-    nbytes = L.ddm_frm_ex_workspace_bytes(H1, W1, H2, W2, d, dt, grid_stride, n, max_iter)
+    mt = METRICS[metric]
+    nbytes = L.ddm_frm_ex_workspace_bytes(H1, W1, H2, W2, d, dt, mt, grid_stride, n, max_iter)
     if nbytes == 0:
         raise DDMError(-1, "ddm_frm_ex_workspace_bytes")
     ws = _workspace(nbytes, dev)
-    _rc(L.ddm_frm_match_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride,
+    _rc(L.ddm_frm_match_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, mt, grid_stride,
                            _ptr(starts) if n >= 0 else None, max(n, 0), max_iter, float(pixel_tol), _ptr(basin),
                            _ptr(out_i), _ptr(out_j), _ptr(out_s), cap, _ptr(count), _ptr(state), _ptr(qc),
                            _ptr(ws), ws.numel(), _stream()), "ddm_frm_match_ex")
@@ -320,7 +334,7 @@ def frm_match_ex(D1: torch.Tensor, D2: torch.Tensor, *, grid_stride: int = 8, st
 
 # ------------------------------------------------------------------- mutual NN
 class MutualBuffers:
-    def __init__(self, H1, W1, H2, W2, d, dtype, device, with_nn=False):
+    def __init__(self, H1, W1, H2, W2, d, dtype, device, with_nn=False, metric: str = "dot"):
         L = lib()
         self.cap = min(H1 * W1, H2 * W2)
         self.out_i = torch.empty(self.cap, dtype=torch.int32, device=device)
@@ -329,9 +343,10 @@ class MutualBuffers:
         self.count = torch.zeros(1, dtype=torch.int32, device=device)
         self.nn12 = torch.empty(H1 * W1, dtype=torch.int32, device=device) if with_nn else None
         self.s12 = torch.empty(H1 * W1, dtype=torch.float32, device=device) if with_nn else None
-        nbytes = L.ddm_mutual_workspace_bytes(H1, W1, H2, W2, d, _DT[dtype])
+        self.metric = METRICS[metric]
+        nbytes = L.ddm_mutual_ex_workspace_bytes(H1, W1, H2, W2, d, _DT[dtype], self.metric)
         if nbytes == 0:
-            raise DDMError(-1, "ddm_mutual_workspace_bytes")
+            raise DDMError(-1, "ddm_mutual_ex_workspace_bytes")
         self.ws = _workspace(nbytes, device)
 
 
@@ -341,17 +356,18 @@ def mutual_nn_into(D1, D2, buf: MutualBuffers):
         raise ValueError("D1 and D2 must share dtype and d")
     H1, W1, d = D1.shape
     H2, W2, _ = D2.shape
-    _rc(lib().ddm_mutual_nn(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, _DT[D1.dtype], _ptr(buf.out_i), _ptr(buf.out_j),
-                            _ptr(buf.out_s), buf.cap, _ptr(buf.count), _ptr(buf.nn12), _ptr(buf.s12), _ptr(buf.ws),
-                            buf.ws.numel(), _stream()), "ddm_mutual_nn")
+    _rc(lib().ddm_mutual_nn_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, _DT[D1.dtype], buf.metric, _ptr(buf.out_i),
+                               _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count), _ptr(buf.nn12),
+                               _ptr(buf.s12), _ptr(buf.ws), buf.ws.numel(), _stream()), "ddm_mutual_nn_ex")
 
 
-def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False):
+def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False, metric: str = "dot"):
     """Exhaustive reciprocal nearest neighbours. Returns (i, j, score) ascending in i
-    (and, with return_nn, NN2 index and score of every pixel of image 1)."""
+    (and, with return_nn, NN2 index and score of every pixel of image 1). metric "l2":
+    fp32 pointmaps by Euclidean distance, scores are squared distances."""
     H1, W1, d = D1.shape
     H2, W2, _ = D2.shape
-    buf = MutualBuffers(H1, W1, H2, W2, d, D1.dtype, D1.device, with_nn=return_nn)
+    buf = MutualBuffers(H1, W1, H2, W2, d, D1.dtype, D1.device, with_nn=return_nn, metric=metric)
     mutual_nn_into(D1, D2, buf)
     n = int(buf.count[0].item())
     res = (buf.out_i[:n].clone(), buf.out_j[:n].clone(), buf.out_s[:n].clone())

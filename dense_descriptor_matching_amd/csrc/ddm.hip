@@ -38,14 +38,24 @@ struct MapFmt {
     int np;        // compile-time pieces per row (0 = runtime, fp32)
     int nkb;       // compile-time K blocks
     int esz;       // bytes per element
-    bool repack;   // rows are copied into a zero-padded [n][ld] buffer first
+    bool repack;   // rows are copied into a prepared [n][ld] buffer first (zero padding or metric rows)
+    bool l2;       // Euclidean metric: fp32 rows of d_in, prepared as d = d_in + 2 (query / reference side)
+    int d_in;      // elements per input row
     int tile_bytes() const { return dtype == DT_F32 ? ld * 16 * 4 : np * 16 * 16; }
     int group() const { return TILE * group_tiles(dtype); }          // references per index group
     int sb_rows() const { return nw_for(dtype) * rq_for(dtype, nkb) * 16; }
 };
 
-bool make_fmt(int dtype, int d, MapFmt *f) {
+bool make_fmt(int dtype, int d, MapFmt *f, int metric = DDM_DOT) {
     if (d < 1 || d > DDM_MAX_D) return false;
+    f->l2 = false; f->d_in = d;
+    if (metric == DDM_L2) {
+        if (dtype != DT_F32 || d + 2 > DDM_MAX_D) return false;
+        f->dtype = DT_F32; f->d = d + 2; f->ld = d + 2; f->np = 0; f->nkb = d + 2 <= 32 ? 8 : 32; f->esz = 4;
+        f->repack = true; f->l2 = true;
+        return true;
+    }
+    if (metric != DDM_DOT) return false;
     f->dtype = dtype; f->d = d;
     if (dtype == DT_F32) {
         f->ld = d; f->np = 0; f->nkb = d <= 32 ? 8 : 32; f->esz = 4; f->repack = false;
@@ -318,8 +328,18 @@ int64_t seed_count(int H, int W, int S) {
 }
 
 // Repack every map of a batch into ld-strided rows when needed.
-int maybe_repack(const MapFmt &f, const void *src, long long rows, void *dst, hipStream_t s, const void **use) {
+// ref_side selects the reference-side rows of the Euclidean metric (ignored otherwise).
+int maybe_repack(const MapFmt &f, const void *src, long long rows, void *dst, hipStream_t s, const void **use,
+                 int ref_side = 0) {
     if (!f.repack) { *use = src; return DDM_OK; }
+    if (f.l2) {
+        const int blocks = (int)std::min<long long>((rows + 255) / 256, 65535);
+        hipLaunchKernelGGL(l2_augment_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s, (const float *)src, f.d_in,
+                           rows, ref_side, (float *)dst);
+        DDM_CHECK_LAUNCH();
+        *use = dst;
+        return DDM_OK;
+    }
     const long long total = rows * f.ld;
     const int blocks = (int)std::min<long long>((total + 255) / 256, 65535);
     hipLaunchKernelGGL(repack_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t *)src, f.d, (uint16_t *)dst,
@@ -336,10 +356,10 @@ struct NnPlan {
     size_t o_part, o_rq, o_rr, total;
 };
 
-int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p) {
+int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p, int metric = DDM_DOT) {
     if (NQ < 1 || M < 1 || N < 1 || N > MAX_PIX || M > MAX_PIX || NQ > MAX_PIX) return DDM_ERR_INVALID;
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
-    if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
+    if (!make_fmt(dtype, d, &p->f, metric)) return DDM_ERR_UNSUPPORTED;
     p->NQ = NQ; p->M = M; p->N = N;
     const int sbr = p->f.sb_rows();
     p->qblocks = (M + sbr - 1) / sbr;
@@ -350,8 +370,8 @@ int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p) {
     p->nchunks = (N + chunk - 1) / chunk;
     Bump b;
     p->o_part = b.take((size_t)p->nchunks * M * 8);
-    p->o_rq = p->f.repack ? b.take((size_t)NQ * p->f.ld * 2) : 0;
-    p->o_rr = p->f.repack ? b.take((size_t)N * p->f.ld * 2) : 0;
+    p->o_rq = p->f.repack ? b.take((size_t)NQ * p->f.ld * p->f.esz) : 0;
+    p->o_rr = p->f.repack ? b.take((size_t)N * p->f.ld * p->f.esz) : 0;
     p->total = b.off;
     return DDM_OK;
 }
@@ -363,7 +383,7 @@ struct FrmPlan {
     int chunk1, chunk2, nch1, nch2, qblocks, nblk;
     long long k_bs, cnt_bs, part_bs;
     size_t o_u, o_v, o_conv, o_score, o_act0, o_act1, o_qr0, o_qr1, o_counts, o_part, o_mj, o_ms, o_bc, o_bo,
-        o_r1, o_r2, o_ctl, o_uprev, o_uiter, o_marks, total;
+        o_r1, o_r2, o_r1b, o_r2b, o_ctl, o_uprev, o_uiter, o_marks, total;
     size_t loop_lds;       // dynamic LDS of the loop kernel
     bool explicit_starts;  // seeds from a caller list (k = its length, an upper bound) instead of the grid
 };
@@ -385,13 +405,13 @@ int frm_chunk(const MapFmt &f, int nref, long long wg_other) {
 
 // n_starts < 0: seeds on the stride-S grid; n_starts >= 0: that many explicit starts (one pair only).
 int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int max_iter, FrmPlan *p,
-             int n_starts = -1) {
+             int n_starts = -1, int metric = DDM_DOT) {
     if (B < 1 || !pix_ok(H1, W1) || !pix_ok(H2, W2)) return DDM_ERR_INVALID;
     if (max_iter < 1 || max_iter > DDM_MAX_ITER) return DDM_ERR_INVALID;
     if (n_starts < 0 && S < 1) return DDM_ERR_INVALID;
     if (n_starts >= 0 && (B != 1 || n_starts > MAX_PIX)) return DDM_ERR_INVALID;
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
-    if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
+    if (!make_fmt(dtype, d, &p->f, metric)) return DDM_ERR_UNSUPPORTED;
     p->B = B; p->H1 = H1; p->W1 = W1; p->N1 = H1 * W1; p->N2 = H2 * W2;
     p->max_iter = max_iter; p->nhalf = 2 * max_iter;
     p->explicit_starts = n_starts >= 0;
@@ -424,8 +444,11 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
     p->o_ms = b.take((size_t)B * p->N1 * 4);
     p->o_bc = b.take((size_t)B * p->nblk * 4);
     p->o_bo = b.take((size_t)B * p->nblk * 4);
-    p->o_r1 = p->f.repack ? b.take((size_t)B * p->N1 * p->f.ld * 2) : 0;
-    p->o_r2 = p->f.repack ? b.take((size_t)B * p->N2 * p->f.ld * 2) : 0;
+    p->o_r1 = p->f.repack ? b.take((size_t)B * p->N1 * p->f.ld * p->f.esz) : 0;
+    p->o_r2 = p->f.repack ? b.take((size_t)B * p->N2 * p->f.ld * p->f.esz) : 0;
+    // the Euclidean metric needs each map on both sides (query and reference rows differ)
+    p->o_r1b = p->f.l2 ? b.take((size_t)B * p->N1 * p->f.ld * p->f.esz) : 0;
+    p->o_r2b = p->f.l2 ? b.take((size_t)B * p->N2 * p->f.ld * p->f.esz) : 0;
     p->o_ctl = b.take(256);
     p->o_uprev = b.take(kb); p->o_uiter = b.take(kb);
     p->o_marks = p->explicit_starts ? b.take((size_t)p->N1 * 4) : 0;
@@ -450,13 +473,15 @@ int compact_run(const int32_t *mj, const float *ms, long long n_bs, int n, int B
 }
 
 // Sweep and resolve arguments of one FRM direction (0: image 1 -> 2, 1: back).
-void frm_dir_args(const FrmPlan &P, const void *m1, const void *m2, uint64_t *part, int dir, SweepArgs *a,
-                  ResolveArgs *r) {
+// m1q/m2q: the maps as queries, m1r/m2r: as references (the same buffers except
+// under the Euclidean metric).
+void frm_dir_args(const FrmPlan &P, const void *m1q, const void *m1r, const void *m2q, const void *m2r,
+                  uint64_t *part, int dir, SweepArgs *a, ResolveArgs *r) {
     const MapFmt &f = P.f;
     const long long b1 = (long long)P.N1 * f.ld * f.esz, b2 = (long long)P.N2 * f.ld * f.esz;
     *a = SweepArgs{};
-    a->Q = (const unsigned char *)(dir == 0 ? m1 : m2);
-    a->R = (const unsigned char *)(dir == 0 ? m2 : m1);
+    a->Q = (const unsigned char *)(dir == 0 ? m1q : m2q);
+    a->R = (const unsigned char *)(dir == 0 ? m2r : m1r);
     a->q_bs = dir == 0 ? b1 : b2;
     a->r_bs = dir == 0 ? b2 : b1;
     a->qrows_bs = P.k_bs;
@@ -476,6 +501,7 @@ void frm_dir_args(const FrmPlan &P, const void *m1, const void *m2, uint64_t *pa
     r->Q = a->Q; r->q_bs = a->q_bs; r->nq = P.k;
     r->R = a->R; r->r_bs = a->r_bs; r->nref = a->nref; r->ld = f.ld; r->d = f.d;
     r->split = split; r->qblocks = P.qblocks; r->split_rows = f.sb_rows(); r->chunk_groups = a->chunk / f.group();
+    r->neg_out = f.l2 ? 1 : 0;
 }
 
 // Half-steps [0, h_loop) run as one sweep and one update launch each, the
@@ -486,11 +512,18 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
             void *ws, hipStream_t s, int h_loop) {
     unsigned char *w = (unsigned char *)ws;
     const MapFmt &f = P.f;
-    const void *m1, *m2;
+    const void *m1, *m2, *m1r, *m2r;
     int rc = maybe_repack(f, D1, (long long)P.B * P.N1, w + P.o_r1, s, &m1);
     if (rc) return rc;
     rc = maybe_repack(f, D2, (long long)P.B * P.N2, w + P.o_r2, s, &m2);
     if (rc) return rc;
+    m1r = m1; m2r = m2;
+    if (f.l2) {
+        rc = maybe_repack(f, D1, (long long)P.B * P.N1, w + P.o_r1b, s, &m1r, 1);
+        if (rc) return rc;
+        rc = maybe_repack(f, D2, (long long)P.B * P.N2, w + P.o_r2b, s, &m2r, 1);
+        if (rc) return rc;
+    }
 
     FrmState st;
     st.u = (int32_t *)(w + P.o_u); st.v = (int32_t *)(w + P.o_v); st.conv = (int32_t *)(w + P.o_conv);
@@ -524,8 +557,8 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
 
     if (P.k > 0) {
         FrmArgs fa{};
-        frm_dir_args(P, m1, m2, part, 0, &fa.sw[0], &fa.rs[0]);
-        frm_dir_args(P, m1, m2, part, 1, &fa.sw[1], &fa.rs[1]);
+        frm_dir_args(P, m1, m1r, m2, m2r, part, 0, &fa.sw[0], &fa.rs[0]);
+        frm_dir_args(P, m1, m1r, m2, m2r, part, 1, &fa.sw[1], &fa.rs[1]);
         fa.st = st; fa.B = P.B; fa.nhalf = P.nhalf; fa.k = P.k; fa.qblocks = P.qblocks;
         fa.nch[0] = P.nch2; fa.nch[1] = P.nch1;
         fa.bar = ctl; fa.err = (int32_t *)(ctl + 32);
@@ -560,10 +593,10 @@ struct MutualPlan {
     size_t o_part, o_col, o_cmax, o_mj, o_ms, o_bc, o_bo, o_r1, o_r2, total;
 };
 
-int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p) {
+int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p, int metric = DDM_DOT) {
     if (!pix_ok(H1, W1) || !pix_ok(H2, W2)) return DDM_ERR_INVALID;
     if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
-    if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
+    if (!make_fmt(dtype, d, &p->f, metric)) return DDM_ERR_UNSUPPORTED;
     p->N1 = H1 * W1; p->N2 = H2 * W2;
     const int sbr = p->f.sb_rows();
     const int nsb = (p->N1 + sbr - 1) / sbr;
@@ -585,8 +618,8 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p)
     p->o_ms = b.take((size_t)p->N1 * 4);
     p->o_bc = b.take((size_t)p->nblk * 4);
     p->o_bo = b.take((size_t)p->nblk * 4);
-    p->o_r1 = p->f.repack ? b.take((size_t)p->N1 * p->f.ld * 2) : 0;
-    p->o_r2 = p->f.repack ? b.take((size_t)p->N2 * p->f.ld * 2) : 0;
+    p->o_r1 = p->f.repack ? b.take((size_t)p->N1 * p->f.ld * p->f.esz) : 0;
+    p->o_r2 = p->f.repack ? b.take((size_t)p->N2 * p->f.ld * p->f.esz) : 0;
     p->total = b.off;
     return DDM_OK;
 }
@@ -713,15 +746,20 @@ int ddm_profile_read(double *total_ms, int64_t *launches) {
 
 extern "C" {
 
-size_t ddm_nn_workspace_bytes(int NQ, int M, int N, int d, int dtype) {
+size_t ddm_nn_ex_workspace_bytes(int NQ, int M, int N, int d, int dtype, int metric) {
     NnPlan P;
-    return nn_plan(NQ, M, N, d, dtype, &P) == DDM_OK ? P.total : 0;
+    return nn_plan(NQ, M, N, d, dtype, &P, metric) == DDM_OK ? P.total : 0;
 }
 
-int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, int N, int d, int dtype,
-           int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+size_t ddm_nn_workspace_bytes(int NQ, int M, int N, int d, int dtype) {
+    return ddm_nn_ex_workspace_bytes(NQ, M, N, d, dtype, DDM_DOT);
+}
+
+int ddm_nn_ex(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, int N, int d, int dtype,
+              int metric, int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes,
+              hipStream_t stream) {
     NnPlan P;
-    int rc = nn_plan(NQ, M, N, d, dtype, &P);
+    int rc = nn_plan(NQ, M, N, d, dtype, &P, metric);
     if (rc) return rc;
     if (!map_ok(Q, P.f) || !map_ok(R, P.f) || !out_idx || !out_score) return DDM_ERR_INVALID;
     if (!q_rows && NQ < M) return DDM_ERR_INVALID;
@@ -731,7 +769,7 @@ int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, i
     const void *q, *r;
     rc = maybe_repack(P.f, Q, NQ, w + P.o_rq, stream, &q);
     if (rc) return rc;
-    rc = maybe_repack(P.f, R, N, w + P.o_rr, stream, &r);
+    rc = maybe_repack(P.f, R, N, w + P.o_rr, stream, &r, 1);
     if (rc) return rc;
     SweepArgs a{};
     a.Q = (const unsigned char *)q; a.R = (const unsigned char *)r; a.qrows = q_rows;
@@ -741,12 +779,19 @@ int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, i
     DDM_CHECK(launch_sweep(P.f, false, a, dim3(P.nchunks, P.qblocks, 1), stream));
     ResolveArgs ra{};
     ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = M;
-    ra.Q = a.Q; ra.qrows = q_rows; ra.nq = M; ra.R = a.R; ra.nref = N; ra.ld = P.f.ld; ra.d = d;
+    ra.Q = a.Q; ra.qrows = q_rows; ra.nq = M; ra.R = a.R; ra.nref = N; ra.ld = P.f.ld; ra.d = P.f.d;
+    ra.neg_out = P.f.l2 ? 1 : 0;
     const int qb = resolve_qb(M);
     DDM_DT_QB_SWITCH(P.f.dtype, qb, nn_resolve_kernel, dim3((M + qb - 1) / qb), dim3(256), 0, stream, ra, out_idx,
                      out_score);
     DDM_CHECK_LAUNCH();
     return DDM_OK;
+}
+
+int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, int N, int d, int dtype,
+           int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return ddm_nn_ex(Q, NQ, q_rows, M, R, N, d, dtype, DDM_DOT, out_idx, out_score, workspace, workspace_bytes,
+                     stream);
 }
 
 size_t ddm_frm_workspace_bytes(int B, int H1, int W1, int H2, int W2, int d, int dtype, int grid_stride,
@@ -756,7 +801,7 @@ size_t ddm_frm_workspace_bytes(int B, int H1, int W1, int H2, int W2, int d, int
 }
 
 static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
-                     int grid_stride, int max_iter, const FrmOpts &O, int32_t *out_i, int32_t *out_j,
+                     int metric, int grid_stride, int max_iter, const FrmOpts &O, int32_t *out_i, int32_t *out_j,
                      float *out_score, int32_t capacity, int32_t *out_count, int32_t *seed_state,
                      int32_t *query_counts, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     FrmPlan P;
@@ -764,7 +809,7 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
     if (!O.starts && O.n_starts != 0) return DDM_ERR_INVALID;
     if (!(O.pixel_tol >= 0.0) || !std::isfinite(O.pixel_tol)) return DDM_ERR_INVALID;
     if (O.pixel_tol > 0.0 && !O.starts) return DDM_ERR_INVALID;       // the routine has no grid form of it
-    int rc = frm_plan(B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P, O.starts ? O.n_starts : -1);
+    int rc = frm_plan(B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P, O.starts ? O.n_starts : -1, metric);
     if (rc) return rc;
     if (!map_ok(D1, P.f) || !map_ok(D2, P.f)) return DDM_ERR_INVALID;
     if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
@@ -783,7 +828,7 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)seed_state,
                           (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, (uint64_t)h_loop,
                           (uint64_t)(uintptr_t)O.starts, (uint64_t)(uint32_t)O.n_starts, tol_bits,
-                          (uint64_t)(uintptr_t)O.basin};
+                          (uint64_t)(uintptr_t)O.basin, (uint64_t)metric};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return frm_run(P, O, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts,
                        workspace, s, h_loop);
@@ -794,7 +839,8 @@ int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2
                   int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
                   int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *workspace,
                   size_t workspace_bytes, hipStream_t stream) {
-    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, FrmOpts{}, out_i, out_j, out_score,
+    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, DDM_DOT, grid_stride, max_iter, FrmOpts{}, out_i, out_j,
+                     out_score,
                      capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
 }
 
@@ -802,19 +848,21 @@ int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2,
                           int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score,
                           int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return frm_entry(B, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, FrmOpts{}, out_i, out_j, out_score,
+    return frm_entry(B, D1, H1, W1, D2, H2, W2, d, dtype, DDM_DOT, grid_stride, max_iter, FrmOpts{}, out_i, out_j,
+                     out_score,
                      capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
 }
 
-size_t ddm_frm_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int grid_stride, int n_starts,
-                                  int max_iter) {
+size_t ddm_frm_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int metric, int grid_stride,
+                                  int n_starts, int max_iter) {
     FrmPlan P;
-    return frm_plan(1, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P, n_starts < 0 ? -1 : n_starts) == DDM_OK
+    return frm_plan(1, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P, n_starts < 0 ? -1 : n_starts,
+                    metric) == DDM_OK
                ? P.total
                : 0;
 }
 
-int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype, int metric,
                      int grid_stride, const int32_t *starts, int n_starts, int max_iter, double pixel_tol,
                      int32_t *basin, int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
                      int32_t *out_count, int32_t *seed_state, int32_t *query_counts, void *workspace,
@@ -822,20 +870,24 @@ int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
     FrmOpts O;
     O.starts = starts; O.n_starts = starts ? n_starts : 0; O.pixel_tol = pixel_tol; O.basin = basin;
     if (!starts && n_starts > 0) return DDM_ERR_INVALID;
-    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, grid_stride, max_iter, O, out_i, out_j, out_score,
+    return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, metric, grid_stride, max_iter, O, out_i, out_j, out_score,
                      capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
 }
 
-size_t ddm_mutual_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype) {
+size_t ddm_mutual_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int metric) {
     MutualPlan P;
-    return mutual_plan(H1, W1, H2, W2, d, dtype, &P) == DDM_OK ? P.total : 0;
+    return mutual_plan(H1, W1, H2, W2, d, dtype, &P, metric) == DDM_OK ? P.total : 0;
 }
 
-int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype, int32_t *out_i,
-                  int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count, int32_t *nn12, float *s12,
-                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+size_t ddm_mutual_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype) {
+    return ddm_mutual_ex_workspace_bytes(H1, W1, H2, W2, d, dtype, DDM_DOT);
+}
+
+int ddm_mutual_nn_ex(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype, int metric,
+                     int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
+                     int32_t *nn12, float *s12, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     MutualPlan P;
-    int rc = mutual_plan(H1, W1, H2, W2, d, dtype, &P);
+    int rc = mutual_plan(H1, W1, H2, W2, d, dtype, &P, metric);
     if (rc) return rc;
     if (!map_ok(D1, P.f) || !map_ok(D2, P.f)) return DDM_ERR_INVALID;
     if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
@@ -847,7 +899,7 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
     const void *m1, *m2;
     rc = maybe_repack(P.f, D1, P.N1, w + P.o_r1, stream, &m1);
     if (rc) return rc;
-    rc = maybe_repack(P.f, D2, P.N2, w + P.o_r2, stream, &m2);
+    rc = maybe_repack(P.f, D2, P.N2, w + P.o_r2, stream, &m2, 1);
     if (rc) return rc;
     SweepArgs a{};
     a.Q = (const unsigned char *)m1; a.R = (const unsigned char *)m2;
@@ -862,7 +914,8 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
     DDM_CHECK_LAUNCH();
     ResolveArgs ra{};
     ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = P.N1;
-    ra.Q = a.Q; ra.nq = P.N1; ra.R = a.R; ra.nref = P.N2; ra.ld = P.f.ld; ra.d = d;
+    ra.Q = a.Q; ra.nq = P.N1; ra.R = a.R; ra.nref = P.N2; ra.ld = P.f.ld; ra.d = P.f.d;
+    ra.neg_out = P.f.l2 ? 1 : 0;
     int32_t *mj = (int32_t *)(w + P.o_mj);
     float *ms = (float *)(w + P.o_ms);
     const int qb = resolve_qb(P.N1);
@@ -871,6 +924,13 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
     DDM_CHECK_LAUNCH();
     return compact_run(mj, ms, P.N1, P.N1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo), out_i, out_j,
                        out_score, capacity, out_count, stream);
+}
+
+int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype, int32_t *out_i,
+                  int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count, int32_t *nn12, float *s12,
+                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return ddm_mutual_nn_ex(D1, H1, W1, D2, H2, W2, d, dtype, DDM_DOT, out_i, out_j, out_score, capacity, out_count,
+                            nn12, s12, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

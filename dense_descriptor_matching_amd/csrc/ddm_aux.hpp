@@ -169,7 +169,10 @@ struct ResolveArgs {
     const int32_t *qcount; long long qcount_bs; int nq;
     const unsigned char *R; long long r_bs; int nref; int ld; int d;
     int split, qblocks, split_rows, chunk_groups;   // runtime split of the sweep (SweepArgs)
+    int neg_out;     // Euclidean metric: report -score (the squared distance, clamped at 0)
 };
+
+__device__ __forceinline__ float reported(float s, int neg_out) { return neg_out ? fmaxf(-s, 0.f) : s; }
 
 // Plain NN output: out_idx[x], out_score[x] for every query.
 template <int DT, int QB>
@@ -181,7 +184,7 @@ __global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, int32_t 
                           return a.Q + (long long)qrow * a.ld * Tr<DT>::ESZ;
                       },
                       [&](bool valid, int x, int j, float s, int sub) {
-                          if (valid && sub == 0) { out_idx[x] = j; out_score[x] = s; }
+                          if (valid && sub == 0) { out_idx[x] = j; out_score[x] = reported(s, a.neg_out); }
                       });
 }
 
@@ -208,9 +211,10 @@ __global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const u
                       [&](bool valid, int x, int j, float s, int sub) {
                           if (valid && sub == 0) {
                               const bool mutual = colmax[j] == fkey(s);
+                              const float rs = reported(s, a.neg_out);
                               match_j[x] = mutual ? j : -1;
-                              match_s[x] = s;
-                              if (nn12) { nn12[x] = j; s12[x] = s; }
+                              match_s[x] = rs;
+                              if (nn12) { nn12[x] = j; s12[x] = rs; }
                           }
                       });
 }
@@ -306,7 +310,7 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
                 if (!backward) {
                     keep = st.basin != nullptr || j != st.v[ko + seed];    // no forward test in the basin variant
                     st.v[ko + seed] = j;
-                    st.score[ko + seed] = s;
+                    st.score[ko + seed] = reported(s, a.neg_out);
                 } else {
                     const int from = st.u[ko + seed];
                     keep = (j != from);
@@ -467,6 +471,25 @@ __global__ void __launch_bounds__(256) compact_scatter_kernel(const int32_t *mat
 
 // Zero-padded copy [n][d] -> [n][ld] for maps whose rows are not a whole
 // number of 16-byte pieces of a supported width.
+// Euclidean metric: rows of d floats become rows of d + 2 whose dot products
+// are minus the squared distances, so the dot-product sweep finds the nearest
+// point and its negated score is the squared distance:
+//   query side     [2x, -|x|^2, 1]
+//   reference side [x, 1, -|x|^2]        (2 q.r - |q|^2 - |r|^2 = -|q - r|^2)
+__global__ void __launch_bounds__(256) l2_augment_kernel(const float *src, int d, long long n, int ref_side,
+                                                         float *dst) {
+    const int ld = d + 2;
+    for (long long r = (long long)blockIdx.x * 256 + threadIdx.x; r < n; r += (long long)gridDim.x * 256) {
+        const float *x = src + r * d;
+        float *o = dst + r * ld;
+        float nrm = 0.f;
+        for (int c = 0; c < d; ++c) nrm = fmaf(x[c], x[c], nrm);
+        for (int c = 0; c < d; ++c) o[c] = ref_side ? x[c] : 2.f * x[c];
+        o[d] = ref_side ? 1.f : -nrm;
+        o[d + 1] = ref_side ? -nrm : 1.f;
+    }
+}
+
 __global__ void __launch_bounds__(256) repack_kernel(const uint16_t *src, int d, uint16_t *dst, int ld, long long n) {
     const long long total = n * ld;
     for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {

@@ -49,6 +49,14 @@ extern "C" {
 
 typedef enum { DDM_F32 = 0, DDM_F16 = 1, DDM_BF16 = 2 } ddm_dtype;
 
+/* Similarity of the *_ex entry points.
+ *   DDM_DOT: NN = arg-max of the dot product (descriptor maps; every other entry point).
+ *   DDM_L2:  NN = arg-min of the Euclidean distance, for 3D points (pointmaps, d = 3), which
+ *            the pages match with K-d trees ("DUSt3R和MASt3R论文阅读", section MASt3R
+ *            matching); here by the same brute-force sweep: fp32 maps only, d <= DDM_MAX_D - 2,
+ *            lowest index on exact ties, reported scores are squared distances (>= 0). */
+typedef enum { DDM_DOT = 0, DDM_L2 = 1 } ddm_metric;
+
 typedef enum {
     DDM_OK = 0,
     DDM_ERR_INVALID = -1,     /* null pointer, bad size, misaligned or bad parameter */
@@ -83,6 +91,11 @@ size_t ddm_nn_workspace_bytes(int NQ, int M, int N, int d, int dtype);
 int ddm_nn(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, int N, int d, int dtype,
            int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes,
            hipStream_t stream);
+/* The same with a metric (ddm_metric); DDM_DOT is exactly ddm_nn. */
+size_t ddm_nn_ex_workspace_bytes(int NQ, int M, int N, int d, int dtype, int metric);
+int ddm_nn_ex(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R, int N, int d, int dtype,
+              int metric, int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes,
+              hipStream_t stream);
 
 /* ---------------------------------------------------------------- FRM ---
  * Fast Reciprocal Matching from the stride-`grid_stride` seed grid of image 1
@@ -137,14 +150,16 @@ int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2,
  *               stops only when its backward query returns the pixel it started the iteration
  *               from) and every backward query of a seed standing at pixel p stores the pixel it
  *               moved to at basin[p]; pixels never left by a backward query hold -1.
+ *   metric      ddm_metric (DDM_L2 for pointmaps; scores are then squared distances).
  *   capacity    >= k (ddm_seed_count for the grid, n_starts for explicit starts).
  *   seed_state  as for ddm_frm_match, with entry 3 = u_old; rows past the number of distinct
  *               starts are -1.
  * The workspace size comes from ddm_frm_ex_workspace_bytes with n_starts = -1 for the grid. */
-size_t ddm_frm_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int grid_stride,
-                                  int n_starts, int max_iter);
+size_t ddm_frm_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int metric,
+                                  int grid_stride, int n_starts, int max_iter);
 int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
-                     int grid_stride, const int32_t *starts, int n_starts, int max_iter, double pixel_tol,
+                     int metric, int grid_stride, const int32_t *starts, int n_starts, int max_iter,
+                     double pixel_tol,
                      int32_t *basin,
                      int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
                      int32_t *seed_state, int32_t *query_counts,
@@ -179,6 +194,12 @@ int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2
                   int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
                   int32_t *nn12, float *s12,
                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* The same with a metric (ddm_metric); DDM_DOT is exactly ddm_mutual_nn. */
+size_t ddm_mutual_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int metric);
+int ddm_mutual_nn_ex(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                     int metric, int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity,
+                     int32_t *out_count, int32_t *nn12, float *s12,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------- kernel timing ---
  * Benchmark aid, off by default. ddm_profile_enable(mask) makes later calls

@@ -100,11 +100,12 @@ def test_frm_rejects_bad_arguments(L):
 
 
 def _frm_ex(L, **kw):
-    a = dict(D1=FAKE, H1=64, W1=48, D2=FAKE, H2=64, W2=48, d=24, dtype=1, S=8, starts=FAKE, n=100, it=1,
-             tol=0.0, basin=None, oi=FAKE, oj=FAKE, os=FAKE, cap=100, cnt=FAKE, st=None, qc=None, ws=FAKE,
+    a = dict(D1=FAKE, H1=64, W1=48, D2=FAKE, H2=64, W2=48, d=24, dtype=1, metric=0, S=8, starts=FAKE, n=100,
+             it=1, tol=0.0, basin=None, oi=FAKE, oj=FAKE, os=FAKE, cap=100, cnt=FAKE, st=None, qc=None, ws=FAKE,
              wsb=1 << 40)
     a.update(kw)
-    return L.ddm_frm_match_ex(a["D1"], a["H1"], a["W1"], a["D2"], a["H2"], a["W2"], a["d"], a["dtype"], a["S"],
+    return L.ddm_frm_match_ex(a["D1"], a["H1"], a["W1"], a["D2"], a["H2"], a["W2"], a["d"], a["dtype"], a["metric"],
+                              a["S"],
                               a["starts"], a["n"], a["it"], a["tol"], a["basin"], a["oi"], a["oj"], a["os"],
                               a["cap"], a["cnt"], a["st"], a["qc"], a["ws"], a["wsb"], None)
 
@@ -123,11 +124,31 @@ def test_frm_ex_rejects_bad_arguments(L):
     assert _frm_ex(L, wsb=16) == -3
     assert _frm_ex(L, D1=FAKE + 2) == -1
     # workspace: explicit starts need room for their marks and states; invalid requests report 0
-    g = L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 8, -1, 10)
+    g = L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, 8, -1, 10)
     assert g == L.ddm_frm_workspace_bytes(1, 64, 48, 64, 48, 24, 1, 8, 10) > 0
-    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 8, 5000, 1) > g
-    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, -1, 10) == 0
-    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, 10, 1) > 0     # stride unused with starts
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, 8, 5000, 1) > g
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, 0, -1, 10) == 0
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 24, 1, 0, 0, 10, 1) > 0     # stride unused with starts
+
+
+def test_metric_validation(L):
+    # the Euclidean metric takes fp32 maps with d + 2 <= 128; unknown metrics are unsupported
+    assert L.ddm_nn_ex_workspace_bytes(100, 100, 1000, 3, 0, 1) > 0
+    assert L.ddm_nn_ex_workspace_bytes(100, 100, 1000, 3, 1, 1) == 0
+    assert L.ddm_nn_ex_workspace_bytes(100, 100, 1000, 127, 0, 1) == 0
+    assert L.ddm_nn_ex_workspace_bytes(100, 100, 1000, 3, 0, 2) == 0
+    assert L.ddm_nn_ex_workspace_bytes(100, 100, 1000, 24, 1, 0) == L.ddm_nn_workspace_bytes(100, 100, 1000, 24, 1)
+    assert L.ddm_mutual_ex_workspace_bytes(64, 48, 64, 48, 3, 0, 1) > 0
+    assert L.ddm_mutual_ex_workspace_bytes(64, 48, 64, 48, 3, 2, 1) == 0
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 3, 0, 1, 8, -1, 10) > 0
+    assert L.ddm_frm_ex_workspace_bytes(64, 48, 64, 48, 3, 1, 1, 8, -1, 10) == 0
+    assert _frm_ex(L, metric=1) == -4                     # fp16 maps under the Euclidean metric
+    assert _frm_ex(L, metric=7) == -4
+    r = L.ddm_nn_ex(FAKE, 100, None, 100, FAKE, 1000, 3, 1, 1, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert r == -4
+    r = L.ddm_mutual_nn_ex(FAKE, 64, 48, FAKE, 64, 48, 3, 0, 3, FAKE, FAKE, FAKE, 3072, FAKE, None, None, FAKE,
+                           1 << 40, None)
+    assert r == -4
 
 
 def test_frm_batched_rejects_bad_batch(L):
