@@ -243,3 +243,90 @@ def mutual(D1: np.ndarray, D2: np.ndarray, metric: str = "dot"):
         raise MemoryError
     return dict(i=oi[:n].copy(), j=oj[:n].copy(), s=os_[:n].copy(), nn12=nn12, s12=s12, m12=m12,
                 nn21=nn21, s21=s21, m21=m21)
+
+
+# ---------------------------------------------------------------------------
+# Coarse-to-fine matching of maps larger than the network's 512 px: the "MASt3R"
+# note on cv-learn.com (section 手法とアーキテクチャ, 粗密マッチング paragraph) says
+# high-resolution images are matched coarsely first, the coarse correspondences
+# guide the matching of enumerated local crops, and the fine matches are mapped
+# back to the original resolution. The steps below are this package's reading
+# of that paragraph (the page gives no further rule):
+#   coarse maps   every factor-th row and column of each map (starting at 0), a
+#                 stand-in for the network run on the downscaled image;
+#   coarse pairs  FRM on the coarse maps (grid seeds), positions scaled back by factor;
+#   image-1 crops the tiling of image 1 by crop_h x crop_w windows, the last window
+#                 of a row / column moved back to end at the border;
+#   image-2 crops for each image-1 crop holding coarse pairs, the window of the same
+#                 size centred on the lower medians of their image-2 x and y (window
+#                 offset = median - size // 2, clamped into image 2);
+#   fine pairs    FRM on every crop pair (grid seeds), mapped to full-resolution
+#                 indices; a pixel claimed by several crops keeps the first crop's
+#                 pair (crops in raster order); pairs ascending in i.
+# ---------------------------------------------------------------------------
+def crop_windows(H1, W1, H2, W2, crop_h, crop_w, x1, y1, x2, y2):
+    """Crop enumeration from full-resolution coarse pair positions (x1, y1) -> (x2, y2).
+    Returns a list of (x0_1, y0_1, x0_2, y0_2, n) in raster order of the image-1 tiling."""
+    x1, y1, x2, y2 = (np.asarray(a, np.int64) for a in (x1, y1, x2, y2))
+    out = []
+    for ty in range(-(-H1 // crop_h)):
+        for tx in range(-(-W1 // crop_w)):
+            y0 = min(ty * crop_h, H1 - crop_h)
+            x0 = min(tx * crop_w, W1 - crop_w)
+            inside = (y1 >= y0) & (y1 < y0 + crop_h) & (x1 >= x0) & (x1 < x0 + crop_w)
+            n = int(inside.sum())
+            if n:
+                mx = int(np.sort(x2[inside])[(n - 1) // 2])
+                my = int(np.sort(y2[inside])[(n - 1) // 2])
+                x02 = min(max(mx - crop_w // 2, 0), W2 - crop_w)
+                y02 = min(max(my - crop_h // 2, 0), H2 - crop_h)
+            else:
+                x02 = y02 = 0
+            out.append((x0, y0, x02, y02, n))
+    return out
+
+
+def coarse_to_fine(F1, F2, *, factor, coarse_stride, coarse_iter, crop_h, crop_w, fine_stride, fine_iter,
+                   tau: float = 1e-4):
+    """Coarse-to-fine FRM (reading above). F1, F2: float64 [H, W, d].
+    Returns dict(i, j, s, crops, coarse=(ci, cj), fine=[per-crop frm results or None])."""
+    F1 = np.asarray(F1, np.float64); F2 = np.asarray(F2, np.float64)
+    H1, W1, d = F1.shape
+    H2, W2, _ = F2.shape
+    if not (1 <= crop_h <= min(H1, H2) and 1 <= crop_w <= min(W1, W2)) or factor < 1:
+        raise ValueError("bad crop size or factor")
+    C1 = np.ascontiguousarray(F1[::factor, ::factor]); C2 = np.ascontiguousarray(F2[::factor, ::factor])
+    Hc1, Wc1 = C1.shape[:2]; Wc2 = C2.shape[1]
+    cr = frm(C1, C2, seed_grid(Hc1, Wc1, coarse_stride), coarse_iter, tau)
+    ci, cj = cr["i"], cr["j"]
+    x1 = (ci % Wc1) * factor; y1 = (ci // Wc1) * factor
+    x2 = (cj % Wc2) * factor; y2 = (cj // Wc2) * factor
+    crops = crop_windows(H1, W1, H2, W2, crop_h, crop_w, x1, y1, x2, y2)
+    fine, per_crop = [], []
+    seeds = seed_grid(crop_h, crop_w, fine_stride)
+    for b, (x01, y01, x02, y02, n) in enumerate(crops):
+        if n == 0:
+            fine.append(None)
+            continue
+        A = np.ascontiguousarray(F1[y01:y01 + crop_h, x01:x01 + crop_w])
+        B = np.ascontiguousarray(F2[y02:y02 + crop_h, x02:x02 + crop_w])
+        r = frm(A, B, seeds, fine_iter, tau)
+        fine.append(r)
+        I = (r["i"] // crop_w + y01) * W1 + (r["i"] % crop_w + x01)
+        J = (r["j"] // crop_w + y02) * W2 + (r["j"] % crop_w + x02)
+        per_crop.append((I, J, r["s"]))
+    i, j, s = merge_first_wins(per_crop)
+    return dict(i=i, j=j, s=s, crops=crops, coarse=(ci, cj), fine=fine)
+
+
+def merge_first_wins(per_crop):
+    """Merge per-crop full-resolution pairs [(I, J, s), ...] given in crop order: a pixel I
+    reported by several crops keeps the first crop's pair. Returns (i, j, s) ascending in i."""
+    owner = {}
+    for I, J, S in per_crop:
+        for a, b, c in zip(np.asarray(I).tolist(), np.asarray(J).tolist(), np.asarray(S).tolist()):
+            if a not in owner:
+                owner[a] = (b, c)
+    keys = sorted(owner)
+    return (np.array(keys, np.int32), np.array([owner[k][0] for k in keys], np.int32),
+            np.array([owner[k][1] for k in keys], np.float64))

@@ -58,6 +58,19 @@ MUTATIONS = {
     "mutual_score_wrong": ("out_s[n] = s12[i];", "out_s[n] = s21[i];"),
 }
 
+# Planted mistakes in the Python part of the oracle (the coarse-to-fine reading).
+PY_MUTATIONS = {
+    "c2f_upper_median": ("mx = int(np.sort(x2[inside])[(n - 1) // 2])", "mx = int(np.sort(x2[inside])[n // 2])"),
+    "c2f_no_clamp_right": ("x02 = min(max(mx - crop_w // 2, 0), W2 - crop_w)", "x02 = max(mx - crop_w // 2, 0)"),
+    "c2f_centre_not_halved": ("y02 = min(max(my - crop_h // 2, 0), H2 - crop_h)",
+                              "y02 = min(max(my - crop_h, 0), H2 - crop_h)"),
+    "c2f_last_crop_wins": ("            if a not in owner:\n", "            if True:\n"),
+    "c2f_factor_ignored": ("x1 = (ci % Wc1) * factor; y1 = (ci // Wc1) * factor",
+                           "x1 = (ci % Wc1); y1 = (ci // Wc1)"),
+    "c2f_last_tile_not_moved": ("x0 = min(tx * crop_w, W1 - crop_w)", "x0 = tx * crop_w"),
+}
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+
 # pins, as callables with fixed arguments
 PINS = [
     P.test_decode_f16_all_patterns,
@@ -83,6 +96,11 @@ PINS = [
     P.test_l2_nn_ties_and_numpy,
     P.test_l2_mutual_matches_numpy,
     lambda: P.test_l2_frm_equals_orbit_derivation(3),
+    P.test_crop_windows_hand_example,
+    P.test_coarse_to_fine_single_crop_is_frm,
+    lambda: P.test_coarse_to_fine_pure_shift(6, -4),
+    P.test_coarse_to_fine_pairs_reciprocal_within_crop,
+    P.test_merge_first_wins_hand_example,
 ]
 
 
@@ -116,12 +134,14 @@ sys.exit(min(M.count_failures(sys.argv[1]), 100))
 """
 
 
-def _failures(so_path):
+def _failures(so_path, py_root=None):
     # A mutant may read or write out of bounds and crash; run it in its own
     # process. A crash counts as a failed pin (the mistake was noticed).
+    # py_root: a directory holding a mutated copy of the oracle package, put first on the path.
     here = os.path.dirname(os.path.abspath(__file__))
     root = os.path.dirname(here)
-    r = subprocess.run([sys.executable, "-c", _RUNNER, so_path, here, root], capture_output=True, text=True,
+    paths = ([py_root] if py_root else []) + [here, root]
+    r = subprocess.run([sys.executable, "-c", _RUNNER, so_path, *paths], capture_output=True, text=True,
                        timeout=600)
     if r.returncode < 0 or r.returncode > 100:
         return 1
@@ -142,3 +162,18 @@ def test_planted_mistake_is_caught(name, tmp_path):
     assert text.count(old) >= 1, f"mutation site for {name} not found"
     mutated = text.replace(old, new, 1)
     assert _failures(_build(mutated, str(tmp_path), name)) >= 1, f"no pin caught mutation {name}"
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTATIONS))
+def test_planted_python_mistake_is_caught(name, tmp_path):
+    with open(PY_SRC) as f:
+        text = f.read()
+    old, new = PY_MUTATIONS[name]
+    assert text.count(old) >= 1, f"mutation site for {name} not found"
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(text.replace(old, new, 1))
+    with open(SRC) as f:
+        so = _build(f.read(), str(tmp_path), "orig")
+    (pkg / "oracle.c").write_text(open(SRC).read())
+    assert _failures(so, str(tmp_path)) >= 1, f"no pin caught mutation {name}"

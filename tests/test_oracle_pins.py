@@ -462,6 +462,96 @@ def test_l2_pure_shift_closed_form():
     assert np.all(r["s"] == 0.0)
 
 
+# ------------------------------------------------------------- coarse-to-fine crops
+def test_crop_windows_hand_example():
+    """Worked by hand: 10 x 10 image 1, 12 x 8 (H x W) image 2, 4 x 4 crops. Tile offsets 0, 4, 6 on
+    both axes (the last tile moved back to the border); lower medians; offsets clamped into image 2."""
+    x1 = [1, 2, 3, 5, 9, 9, 8]
+    y1 = [1, 2, 0, 1, 9, 8, 5]
+    x2 = [7, 2, 5, 0, 3, 4, 7]
+    y2 = [1, 9, 4, 9, 6, 5, 11]
+    c = oracle.crop_windows(10, 10, 12, 8, 4, 4, x1, y1, x2, y2)
+    assert c == [(0, 0, 3, 2, 3),       # pairs 0-2: medians x 5, y 4 -> (3, 2)
+                 (4, 0, 0, 7, 1),       # pair 3 alone: x 0 - 2 -> 0, y 9 - 2 = 7
+                 (6, 0, 0, 0, 0),       # empty
+                 (0, 4, 0, 0, 0), (4, 4, 0, 0, 0),
+                 (6, 4, 4, 8, 1),       # pair 6: x 7 - 2 = 5 -> 4 (= 8 - 4), y 11 - 2 = 9 -> 8 (= 12 - 4)
+                 (0, 6, 0, 0, 0), (4, 6, 0, 0, 0),
+                 (6, 6, 1, 3, 2)]       # pairs 4, 5: lower medians x 3, y 5 -> (1, 3)
+
+
+def test_coarse_to_fine_single_crop_is_frm():
+    """factor 1 and one crop covering the whole map: the fine stage is plain FRM on the maps."""
+    A = synth.random_map(24, 20, 8, synth.F16, 95).astype(np.float64)
+    B = synth.random_map(24, 20, 8, synth.F16, 96).astype(np.float64)
+    r = oracle.coarse_to_fine(A, B, factor=1, coarse_stride=3, coarse_iter=10, crop_h=24, crop_w=20,
+                              fine_stride=2, fine_iter=10)
+    f = oracle.frm(A, B, oracle.seed_grid(24, 20, 2), 10)
+    if r["crops"][0][4] > 0:
+        assert r["crops"] == [(0, 0, 0, 0, r["crops"][0][4])]
+        assert np.array_equal(r["i"], f["i"]) and np.array_equal(r["j"], f["j"])
+
+
+@pytest.mark.parametrize("dx,dy", [(6, -4), (-4, 10)])
+def test_coarse_to_fine_pure_shift(dx, dy):
+    """sigma = 0: every fine seed whose counterpart (x - dx, y - dy) lies inside its image-2 crop ends
+    on that counterpart, and the first crop holding a pixel reports it. (Even shifts: every other
+    pixel of an i.i.d. map keeps its counterpart after subsampling by 2.)"""
+    H, W, ch, cw, S = 96, 80, 48, 40, 4
+    p = synth.make_pair(H, W, 24, synth.F16, 97, sigma=0.0, shift=(dx, dy))
+    A = oracle.decode(p.D1, p.dtype); B = oracle.decode(p.D2, p.dtype)
+    r = oracle.coarse_to_fine(A, B, factor=2, coarse_stride=4, coarse_iter=10, crop_h=ch, crop_w=cw,
+                              fine_stride=S, fine_iter=10)
+    got = dict(zip(r["i"].tolist(), r["j"].tolist()))
+    seen, n_checked = set(), 0
+    for (x01, y01, x02, y02, n) in r["crops"]:
+        if n == 0:
+            continue
+        for q in oracle.seed_grid(ch, cw, S).tolist():
+            x, y = q % cw + x01, q // cw + y01
+            I = y * W + x
+            if I in seen:
+                continue
+            seen.add(I)
+            cx, cy = x - dx, y - dy
+            if x02 <= cx < x02 + cw and y02 <= cy < y02 + ch:
+                assert got.get(I) == cy * W + cx, (I, got.get(I))
+                n_checked += 1
+    assert n_checked > 300
+    assert np.all(np.diff(r["i"]) > 0)
+
+
+def test_merge_first_wins_hand_example():
+    i, j, s = oracle.merge_first_wins([(np.array([7, 3]), np.array([70, 30]), np.array([0.7, 0.3])),
+                                       (np.array([3, 9, 7]), np.array([31, 90, 71]), np.array([.31, .9, .71])),
+                                       (np.array([1]), np.array([10]), np.array([0.1]))])
+    assert i.tolist() == [1, 3, 7, 9] and j.tolist() == [10, 30, 70, 90]
+    assert s.tolist() == [0.1, 0.3, 0.7, 0.9]
+
+
+def test_coarse_to_fine_pairs_reciprocal_within_crop():
+    """Overlapping crops (68 x 52 tiled by 32 x 24): every reported pair is reciprocal inside the
+    first crop (raster order) that holds its image-1 pixel."""
+    p = synth.make_pair(68, 52, 16, synth.F16, 98, sigma=0.15, shift=(6, 4))
+    A = oracle.decode(p.D1, p.dtype); B = oracle.decode(p.D2, p.dtype)
+    r = oracle.coarse_to_fine(A, B, factor=2, coarse_stride=2, coarse_iter=10, crop_h=32, crop_w=24,
+                              fine_stride=2, fine_iter=10)
+    W = 52
+    recip = set()           # full-resolution pairs reciprocal inside some crop pair (numpy NN)
+    for b, (x01, y01, x02, y02, n) in enumerate(r["crops"]):
+        if n == 0:
+            continue
+        ca = A[y01:y01 + 32, x01:x01 + 24].reshape(-1, 16); cb = B[y02:y02 + 32, x02:x02 + 24].reshape(-1, 16)
+        n12 = _np_nn(ca, cb)[0]; n21 = _np_nn(cb, ca)[0]
+        for i in range(ca.shape[0]):
+            j = n12[i]
+            if n21[j] == i:
+                recip.add(((i // 24 + y01) * W + i % 24 + x01, (j // 24 + y02) * W + j % 24 + x02))
+    assert len(r["i"]) > 100 and np.all(np.diff(r["i"]) > 0)
+    for I, J in zip(r["i"].tolist(), r["j"].tolist()):
+        assert (I, J) in recip
+
+
 # --------------------------------------------------------------------- mutual
 @pytest.mark.parametrize("s1,s2,d,seed", [((10, 12), (10, 12), 24, 51), ((7, 9), (11, 5), 3, 52),
                                           ((16, 16), (16, 16), 2, 53)])
