@@ -65,6 +65,9 @@ def _declare(lib):
     lib.ddm_mutual_nn_ex.argtypes = [P, I, I, P, I, I, I, I, I, P, P, P, I, P, P, P, P, SZ, P]
     lib.ddm_mutual_nn_ex.restype = I
     lib.ddm_frm_match_ex.restype = I
+    lib.ddm_c2f_workspace_bytes.argtypes = [I] * 13; lib.ddm_c2f_workspace_bytes.restype = SZ
+    lib.ddm_c2f_match.argtypes = [P, I, I, P, I, I, I, I, I, I, I, I, I, I, I, P, P, P, I, P, P, P, SZ, P]
+    lib.ddm_c2f_match.restype = I
     lib.ddm_frm_set_mode.argtypes = [I]; lib.ddm_frm_set_mode.restype = I
     lib.ddm_frm_get_mode.argtypes = []; lib.ddm_frm_get_mode.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
@@ -332,6 +335,42 @@ def frm_match_ex(D1: torch.Tensor, D2: torch.Tensor, *, grid_stride: int = 8, st
     return res
 
 
+# ------------------------------------------------------------------- coarse-to-fine
+def c2f_match(F1: torch.Tensor, F2: torch.Tensor, *, factor: int = 2, coarse_stride: int = 8, coarse_iter: int = 10,
+              crop=(512, 384), fine_stride: int = 8, fine_iter: int = 10, return_crops: bool = False):
+    """Coarse-to-fine FRM of maps larger than a crop: coarse FRM on maps subsampled by ``factor``,
+    image-1 tiles of size ``crop`` (H, W), image-2 crops centred on the median coarse target of each
+    tile, batched fine FRM on the crop pairs, fine matches mapped back to full resolution (first
+    tile wins). Returns (i, j, score) [+ crops int32 [tiles, 5]: x0_1, y0_1, x0_2, y0_2, n_coarse]."""
+    _check_map(F1, "F1"); _check_map(F2, "F2")
+    if F1.dtype != F2.dtype or F1.shape[-1] != F2.shape[-1] or F1.dim() != 3 or F2.dim() != 3:
+        raise ValueError("F1, F2 must be [H, W, d] maps of one dtype and d")
+    H1, W1, d = F1.shape
+    H2, W2, _ = F2.shape
+    ch, cw = crop
+    dev = F1.device
+    L = lib()
+    dt = _DT[F1.dtype]
+    nbytes = L.ddm_c2f_workspace_bytes(H1, W1, H2, W2, d, dt, factor, coarse_stride, coarse_iter, ch, cw,
+                                       fine_stride, fine_iter)
+    if nbytes == 0:
+        raise DDMError(-1, "ddm_c2f_workspace_bytes (bad sizes, crop, dtype or d)")
+    tiles = (-(-H1 // ch)) * (-(-W1 // cw))
+    cap = max(1, min(H1 * W1, tiles * seed_count(ch, cw, fine_stride)))
+    out_i = torch.empty(cap, dtype=torch.int32, device=dev)
+    out_j = torch.empty(cap, dtype=torch.int32, device=dev)
+    out_s = torch.empty(cap, dtype=torch.float32, device=dev)
+    count = torch.zeros(1, dtype=torch.int32, device=dev)
+    crops = torch.empty(tiles * 5, dtype=torch.int32, device=dev)
+    ws = _workspace(nbytes, dev)
+    _rc(L.ddm_c2f_match(_ptr(F1), H1, W1, _ptr(F2), H2, W2, d, dt, factor, coarse_stride, coarse_iter, ch, cw,
+                        fine_stride, fine_iter, _ptr(out_i), _ptr(out_j), _ptr(out_s), cap, _ptr(count),
+                        _ptr(crops), _ptr(ws), ws.numel(), _stream()), "ddm_c2f_match")
+    n = _count(count[0].item())
+    res = (out_i[:n].clone(), out_j[:n].clone(), out_s[:n].clone())
+    return res + (crops.view(tiles, 5),) if return_crops else res
+
+
 # ------------------------------------------------------------------- mutual NN
 class MutualBuffers:
     def __init__(self, H1, W1, H2, W2, d, dtype, device, with_nn=False, metric: str = "dot"):
@@ -376,6 +415,6 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False, metri
     return res
 
 
-__all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "mutual_nn", "mutual_nn_into", "seed_count",
+__all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "c2f_match", "mutual_nn", "mutual_nn_into", "seed_count",
            "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH", "profile_enable", "profile_read",
            "frm_set_mode", "frm_get_mode", "FRM_PER_HALF_STEP", "FRM_LOOP"]

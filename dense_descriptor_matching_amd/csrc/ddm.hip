@@ -4,6 +4,7 @@
 // the host only checks arguments and enqueues.
 #include "../../include/ddm.h"
 #include "ddm_frm.hpp"
+#include "ddm_c2f.hpp"
 
 #include <algorithm>
 #include <cmath>
@@ -586,6 +587,110 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
                        (const int32_t *)(ctl + 32));
 }
 
+// ------------------------------------------------------ coarse-to-fine plan
+struct C2fPlan {
+    MapFmt f;
+    int H1, W1, H2, W2, d, dtype, factor, Hc1, Wc1, Hc2, Wc2, CH, CW, ntx, nty, ntiles, words;
+    int kc, kf, nblk;
+    FrmPlan pc, pf;           // coarse FRM (one pair) and fine FRM (one pair per tile)
+    size_t o_c1, o_c2, o_cws, o_ci, o_cj, o_cs, o_cc, o_info, o_b1, o_b2, o_fws, o_fi, o_fj, o_fs, o_fc, o_owner,
+        o_mj, o_ms, o_bc, o_bo, total;
+    CropGeom geom() const {
+        return CropGeom{H1, W1, H2, W2, CH, CW, ntx, nty, factor, Wc1, Wc2};
+    }
+};
+
+int c2f_plan(int H1, int W1, int H2, int W2, int d, int dtype, int factor, int cs, int cit, int CH, int CW, int fs,
+             int fit, C2fPlan *p) {
+    if (!pix_ok(H1, W1) || !pix_ok(H2, W2) || factor < 1) return DDM_ERR_INVALID;
+    if (CH < 1 || CW < 1 || CH > H1 || CH > H2 || CW > W1 || CW > W2) return DDM_ERR_INVALID;
+    if (dtype != DT_F32 && dtype != DT_F16 && dtype != DT_BF16) return DDM_ERR_UNSUPPORTED;
+    if (!make_fmt(dtype, d, &p->f)) return DDM_ERR_UNSUPPORTED;
+    if ((d * p->f.esz) % 4 != 0) return DDM_ERR_UNSUPPORTED;           // crops move whole 32-bit words
+    if ((long long)W2 + H2 + 1 > 16384) return DDM_ERR_UNSUPPORTED;     // median histograms live in LDS
+    p->H1 = H1; p->W1 = W1; p->H2 = H2; p->W2 = W2; p->d = d; p->dtype = dtype; p->factor = factor;
+    p->Hc1 = (H1 + factor - 1) / factor; p->Wc1 = (W1 + factor - 1) / factor;
+    p->Hc2 = (H2 + factor - 1) / factor; p->Wc2 = (W2 + factor - 1) / factor;
+    p->CH = CH; p->CW = CW;
+    p->nty = (H1 + CH - 1) / CH; p->ntx = (W1 + CW - 1) / CW; p->ntiles = p->nty * p->ntx;
+    p->words = d * p->f.esz / 4;
+    int rc = frm_plan(1, p->Hc1, p->Wc1, p->Hc2, p->Wc2, d, dtype, cs, cit, &p->pc);
+    if (rc) return rc;
+    rc = frm_plan(p->ntiles, CH, CW, CH, CW, d, dtype, fs, fit, &p->pf);
+    if (rc) return rc;
+    p->kc = std::max(p->pc.k, 1); p->kf = std::max(p->pf.k, 1);
+    p->nblk = (H1 * W1 + CB - 1) / CB;
+    const size_t row = (size_t)d * p->f.esz;
+    Bump b;
+    p->o_c1 = b.take((size_t)p->Hc1 * p->Wc1 * row);
+    p->o_c2 = b.take((size_t)p->Hc2 * p->Wc2 * row);
+    p->o_cws = b.take(p->pc.total);
+    p->o_ci = b.take((size_t)p->kc * 4); p->o_cj = b.take((size_t)p->kc * 4); p->o_cs = b.take((size_t)p->kc * 4);
+    p->o_cc = b.take(4);
+    p->o_info = b.take((size_t)p->ntiles * 5 * 4);
+    p->o_b1 = b.take((size_t)p->ntiles * CH * CW * row);
+    p->o_b2 = b.take((size_t)p->ntiles * CH * CW * row);
+    p->o_fws = b.take(p->pf.total);
+    const size_t nf = (size_t)p->ntiles * p->kf;
+    p->o_fi = b.take(nf * 4); p->o_fj = b.take(nf * 4); p->o_fs = b.take(nf * 4);
+    p->o_fc = b.take((size_t)p->ntiles * 4);
+    const size_t n1 = (size_t)H1 * W1;
+    p->o_owner = b.take(n1 * 4); p->o_mj = b.take(n1 * 4); p->o_ms = b.take(n1 * 4);
+    p->o_bc = b.take((size_t)p->nblk * 4); p->o_bo = b.take((size_t)p->nblk * 4);
+    p->total = b.off;
+    return DDM_OK;
+}
+
+int c2f_run(const C2fPlan &P, const void *F1, const void *F2, int32_t *out_i, int32_t *out_j, float *out_score,
+            int32_t capacity, int32_t *out_count, int32_t *crop_info, void *ws, hipStream_t s, int h_loop_mode) {
+    unsigned char *w = (unsigned char *)ws;
+    const CropGeom g = P.geom();
+    // coarse maps and coarse FRM
+    const long long nc1 = (long long)P.Hc1 * P.Wc1 * P.words, nc2 = (long long)P.Hc2 * P.Wc2 * P.words;
+    hipLaunchKernelGGL(subsample_kernel, dim3((int)std::min<long long>((nc1 + 255) / 256, 4096)), dim3(256), 0, s,
+                       (const uint32_t *)F1, P.W1, P.words, P.factor, P.Hc1, P.Wc1, (uint32_t *)(w + P.o_c1));
+    DDM_CHECK_LAUNCH();
+    hipLaunchKernelGGL(subsample_kernel, dim3((int)std::min<long long>((nc2 + 255) / 256, 4096)), dim3(256), 0, s,
+                       (const uint32_t *)F2, P.W2, P.words, P.factor, P.Hc2, P.Wc2, (uint32_t *)(w + P.o_c2));
+    DDM_CHECK_LAUNCH();
+    int32_t *ci = (int32_t *)(w + P.o_ci), *cj = (int32_t *)(w + P.o_cj), *cc = (int32_t *)(w + P.o_cc);
+    int rc = frm_run(P.pc, FrmOpts{}, w + P.o_c1, w + P.o_c2, ci, cj, (float *)(w + P.o_cs), P.kc, cc, nullptr,
+                     nullptr, w + P.o_cws, s, h_loop_mode ? 0 : P.pc.nhalf);
+    if (rc) return rc;
+    // crop windows, crop batches, fine FRM
+    int32_t *info = crop_info ? crop_info : (int32_t *)(w + P.o_info);
+    const size_t hist = (size_t)(P.W2 + P.H2 + 1) * sizeof(int);
+    hipLaunchKernelGGL(crop_stats_kernel, dim3(P.ntiles), dim3(256), hist, s, (const int32_t *)ci,
+                       (const int32_t *)cj, (const int32_t *)cc, g, info);
+    DDM_CHECK_LAUNCH();
+    const long long per = (long long)P.CH * P.CW * P.words;
+    hipLaunchKernelGGL(crop_gather_kernel, dim3((int)std::min<long long>((per + 255) / 256, 2048), P.ntiles),
+                       dim3(256), 0, s, (const uint32_t *)F1, (const uint32_t *)F2, P.words, g,
+                       (const int32_t *)info, (uint32_t *)(w + P.o_b1), (uint32_t *)(w + P.o_b2));
+    DDM_CHECK_LAUNCH();
+    int32_t *fi = (int32_t *)(w + P.o_fi), *fj = (int32_t *)(w + P.o_fj), *fc = (int32_t *)(w + P.o_fc);
+    float *fsc = (float *)(w + P.o_fs);
+    rc = frm_run(P.pf, FrmOpts{}, w + P.o_b1, w + P.o_b2, fi, fj, fsc, P.kf, fc, nullptr, nullptr, w + P.o_fws, s,
+                 h_loop_mode ? 0 : P.pf.nhalf);
+    if (rc) return rc;
+    // merge into full resolution, first tile wins, ordered output
+    const int n1 = P.H1 * P.W1;
+    int32_t *owner = (int32_t *)(w + P.o_owner), *mj = (int32_t *)(w + P.o_mj);
+    float *ms = (float *)(w + P.o_ms);
+    hipLaunchKernelGGL(c2f_clear_kernel, dim3(std::min((n1 + 255) / 256, 4096)), dim3(256), 0, s, owner, mj, n1);
+    DDM_CHECK_LAUNCH();
+    const dim3 mg((unsigned)std::min((P.kf + 255) / 256, 1024), (unsigned)P.ntiles);
+    hipLaunchKernelGGL(crop_owner_kernel, mg, dim3(256), 0, s, (const int32_t *)fi, (const int32_t *)fc, P.kf, g,
+                       (const int32_t *)info, owner);
+    DDM_CHECK_LAUNCH();
+    hipLaunchKernelGGL(crop_write_kernel, mg, dim3(256), 0, s, (const int32_t *)fi, (const int32_t *)fj,
+                       (const float *)fsc, (const int32_t *)fc, P.kf, g, (const int32_t *)info,
+                       (const int32_t *)owner, mj, ms);
+    DDM_CHECK_LAUNCH();
+    return compact_run(mj, ms, n1, n1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo), out_i, out_j,
+                       out_score, capacity, out_count, s);
+}
+
 // -------------------------------------------------------------- mutual plan
 struct MutualPlan {
     MapFmt f;
@@ -872,6 +977,44 @@ int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
     if (!starts && n_starts > 0) return DDM_ERR_INVALID;
     return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, metric, grid_stride, max_iter, O, out_i, out_j, out_score,
                      capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
+}
+
+size_t ddm_c2f_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int factor, int coarse_stride,
+                               int coarse_iter, int crop_h, int crop_w, int fine_stride, int fine_iter) {
+    C2fPlan P;
+    return c2f_plan(H1, W1, H2, W2, d, dtype, factor, coarse_stride, coarse_iter, crop_h, crop_w, fine_stride,
+                    fine_iter, &P) == DDM_OK
+               ? P.total
+               : 0;
+}
+
+int ddm_c2f_match(const void *F1, int H1, int W1, const void *F2, int H2, int W2, int d, int dtype, int factor,
+                  int coarse_stride, int coarse_iter, int crop_h, int crop_w, int fine_stride, int fine_iter,
+                  int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
+                  int32_t *crop_info, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    C2fPlan P;
+    int rc = c2f_plan(H1, W1, H2, W2, d, dtype, factor, coarse_stride, coarse_iter, crop_h, crop_w, fine_stride,
+                      fine_iter, &P);
+    if (rc) return rc;
+    if (!map_ok(F1, P.f) || !map_ok(F2, P.f) || ((uintptr_t)F1 | (uintptr_t)F2) % 4 != 0) return DDM_ERR_INVALID;
+    if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
+    if ((long long)capacity < std::min<long long>((long long)H1 * W1, (long long)P.ntiles * P.pf.k))
+        return DDM_ERR_CAPACITY;
+    if (!workspace || workspace_bytes < P.total) return DDM_ERR_WORKSPACE;
+    if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DDM_ERR_HIP;
+    const int loop = (frm_mode() == DDM_FRM_LOOP && cooperative_ok(dev)) ? 1 : 0;
+    const GraphKey key = {(uint64_t)dev, 0xC2F, (uint64_t)(uintptr_t)F1, (uint64_t)H1, (uint64_t)W1,
+                          (uint64_t)(uintptr_t)F2, (uint64_t)H2, (uint64_t)W2, (uint64_t)d, (uint64_t)dtype,
+                          (uint64_t)factor, (uint64_t)coarse_stride, (uint64_t)coarse_iter, (uint64_t)crop_h,
+                          (uint64_t)crop_w, (uint64_t)fine_stride, (uint64_t)fine_iter, (uint64_t)(uintptr_t)out_i,
+                          (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
+                          (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)crop_info,
+                          (uint64_t)(uintptr_t)workspace, (uint64_t)loop};
+    return run_graphed(key, stream, [&](hipStream_t s) {
+        return c2f_run(P, F1, F2, out_i, out_j, out_score, capacity, out_count, crop_info, workspace, s, loop);
+    });
 }
 
 size_t ddm_mutual_ex_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int metric) {

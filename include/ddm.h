@@ -183,6 +183,34 @@ typedef enum { DDM_FRM_PER_HALF_STEP = 0, DDM_FRM_LOOP = 1 } ddm_frm_mode;
 int ddm_frm_set_mode(int mode);
 int ddm_frm_get_mode(void);
 
+/* ----------------------------------------------------- coarse-to-fine ---
+ * Matching of maps larger than the network's 512-px input ("MASt3R" note on cv-learn.com,
+ * section 手法とアーキテクチャ, 粗密マッチング paragraph: coarse matching first, the coarse
+ * correspondences guide the matching of enumerated local crops, fine matches mapped back to
+ * the original resolution). Steps, as read here (the page gives no further rule):
+ *   1. coarse maps: every `factor`-th row and column of F1 and F2 (from 0);
+ *   2. coarse pairs: FRM on them (grid stride coarse_stride, coarse_iter iterations);
+ *   3. image-1 crops: the tiling of image 1 by crop_h x crop_w windows, raster order, the last
+ *      window of a row / column moved back to end at the border;
+ *   4. image-2 crop of each tile: same size, centred on the lower medians of the image-2 x and y
+ *      (full resolution) of the coarse pairs whose image-1 pixel lies in the tile (offset =
+ *      median - size / 2, clamped into image 2); tiles without coarse pairs are skipped;
+ *   5. fine pairs: FRM on every crop pair (grid stride fine_stride, fine_iter iterations), mapped
+ *      to full-resolution indices; a pixel reported by several tiles keeps the first tile's pair.
+ * Outputs as for ddm_frm_match (unique, ascending in i, fp32 dot products);
+ * capacity >= min(H1*W1, tiles * ddm_seed_count(crop_h, crop_w, fine_stride)).
+ *   crop_info  device int32[tiles][5] or NULL: x0_1, y0_1, x0_2, y0_2, coarse pairs in the tile.
+ * Requires crop sizes within both maps, factor >= 1, d * element size a multiple of 4 bytes,
+ * W2 + H2 < 16384. FRM calls inside follow ddm_frm_set_mode. */
+size_t ddm_c2f_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int factor,
+                               int coarse_stride, int coarse_iter, int crop_h, int crop_w,
+                               int fine_stride, int fine_iter);
+int ddm_c2f_match(const void *F1, int H1, int W1, const void *F2, int H2, int W2, int d, int dtype,
+                  int factor, int coarse_stride, int coarse_iter, int crop_h, int crop_w,
+                  int fine_stride, int fine_iter,
+                  int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
+                  int32_t *crop_info, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------- mutual NN ---
  * Exhaustive reciprocal nearest neighbours M (ascending in i), computed in a
  * single pass over all N1 x N2 scores with row arg-max and column max fused.

@@ -151,6 +151,27 @@ def test_metric_validation(L):
     assert r == -4
 
 
+def test_c2f_rejects_bad_arguments(L):
+    def c(**kw):
+        a = dict(F1=FAKE, H1=1024, W1=768, F2=FAKE, H2=1024, W2=768, d=24, dtype=1, f=2, cs=8, ci=10, ch=512, cw=384,
+                 fs=8, fi=10, oi=FAKE, oj=FAKE, os=FAKE, cap=1 << 20, cnt=FAKE, info=None, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return L.ddm_c2f_match(a["F1"], a["H1"], a["W1"], a["F2"], a["H2"], a["W2"], a["d"], a["dtype"], a["f"],
+                               a["cs"], a["ci"], a["ch"], a["cw"], a["fs"], a["fi"], a["oi"], a["oj"], a["os"],
+                               a["cap"], a["cnt"], a["info"], a["ws"], a["wsb"], None)
+    assert c(f=0) == -1
+    assert c(ch=1025) == -1 and c(cw=0) == -1 and c(H2=500) == -1
+    assert c(cs=0) == -1 and c(fi=0) == -1
+    assert c(d=23) == -4                                   # rows must be whole 32-bit words
+    assert c(W2=20000, H2=600) == -4                       # median histograms would not fit in LDS
+    assert c(cap=100) == -2                                # 4 tiles x 3072 fine seeds
+    assert c(wsb=16) == -3
+    assert c(F1=FAKE + 2) == -1
+    assert L.ddm_c2f_workspace_bytes(1024, 768, 1024, 768, 24, 1, 2, 8, 10, 512, 384, 8, 10) > 0
+    assert L.ddm_c2f_workspace_bytes(1024, 768, 1024, 768, 24, 1, 2, 8, 10, 1024, 384, 8, 10) > 0
+    assert L.ddm_c2f_workspace_bytes(1024, 768, 1024, 768, 24, 1, 2, 8, 10, 1025, 384, 8, 10) == 0
+
+
 def test_frm_batched_rejects_bad_batch(L):
     r = L.ddm_frm_match_batched(0, FAKE, 64, 48, FAKE, 64, 48, 24, 1, 8, 10, FAKE, FAKE, FAKE, 48, FAKE, None,
                                 None, FAKE, 1 << 40, None)

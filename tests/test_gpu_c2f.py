@@ -1,0 +1,93 @@
+"""GPU parity of coarse-to-fine crop matching (ddm_c2f_match) against the
+oracle's reading: crop windows, and the merged full-resolution pairs.
+
+When no coarse or fine seed met a margin below tau, the crop windows and the
+pairs must be identical; otherwise the crop windows of tiles whose coarse pairs
+all stayed sharp must agree, and every GPU pair must be reciprocal inside its
+crop pair within tau.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import TAU, exact_scores
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ddm():
+    import dense_descriptor_matching_amd as m
+    m.lib()
+    return m
+
+
+def dev(a, dtype):
+    from synth.torchio import to_device
+    return to_device(a, dtype, "cuda")
+
+
+CASES = [
+    # (H, W, d, dtype, seed, shift, sigma, factor, coarse stride, crop (h, w), fine stride)
+    (256, 192, 24, synth.F16, 301, (12, -8), 0.1, 2, 4, (128, 96), 4),
+    (300, 200, 24, synth.F16, 302, (-10, 6), 0.1, 2, 4, (128, 96), 4),       # overlapping tiles
+    (192, 160, 16, synth.BF16, 303, (8, 8), 0.05, 4, 2, (96, 64), 4),
+    (160, 128, 8, synth.F32, 304, (0, 0), 0.0, 2, 4, (160, 128), 4),         # one crop = the whole map
+    (1024, 768, 24, synth.F16, 305, (34, -18), 0.1, 2, 8, (512, 384), 8),    # 4 crops of the benchmark size
+]
+
+
+@pytest.mark.parametrize("H,W,d,dt,seed,shift,sigma,factor,cs,crop,fs", CASES)
+def test_c2f_against_oracle(ddm, H, W, d, dt, seed, shift, sigma, factor, cs, crop, fs):
+    p = synth.make_pair(H, W, d, dt, seed, sigma=sigma, shift=shift)
+    A, B = oracle.decode(p.D1, p.dtype), oracle.decode(p.D2, p.dtype)
+    ref = oracle.coarse_to_fine(A, B, factor=factor, coarse_stride=cs, coarse_iter=10, crop_h=crop[0],
+                                crop_w=crop[1], fine_stride=fs, fine_iter=10)
+    gi, gj, gs, crops = ddm.c2f_match(dev(p.D1, p.dtype), dev(p.D2, p.dtype), factor=factor, coarse_stride=cs,
+                                      coarse_iter=10, crop=crop, fine_stride=fs, fine_iter=10, return_crops=True)
+    gi, gj, gs, crops = (t.cpu().numpy() for t in (gi, gj, gs, crops))
+    # ambiguity of the coarse stage: the oracle's coarse FRM on the subsampled maps
+    C1 = A[::factor, ::factor]; C2 = B[::factor, ::factor]
+    cr = oracle.frm(np.ascontiguousarray(C1), np.ascontiguousarray(C2),
+                    oracle.seed_grid(C1.shape[0], C1.shape[1], cs), 10)
+    coarse_sharp = not cr["ambiguous"].any()
+    fine_sharp = all(f is None or not f["ambiguous"].any() for f in ref["fine"])
+    if coarse_sharp:
+        assert [tuple(c) for c in crops.tolist()] == ref["crops"]
+    assert np.all(np.diff(gi) > 0)
+    np.testing.assert_allclose(gs, exact_scores(A, B, gi, gj), atol=TAU, rtol=0)
+    if coarse_sharp and fine_sharp:
+        assert gi.tolist() == ref["i"].tolist() and gj.tolist() == ref["j"].tolist()
+    else:
+        # every GPU pair is reciprocal (within tau) inside the first tile of its pixel that reports it
+        Wi, Wj = A.shape[1], B.shape[1]
+        for I, J in zip(gi[:400].tolist(), gj[:400].tolist()):
+            x, y = I % Wi, I // Wi
+            ok = False
+            for (x01, y01, x02, y02, n) in crops.tolist():
+                if n and x01 <= x < x01 + crop[1] and y01 <= y < y01 + crop[0]:
+                    ca = A[y01:y01 + crop[0], x01:x01 + crop[1]].reshape(-1, d)
+                    cb = B[y02:y02 + crop[0], x02:x02 + crop[1]].reshape(-1, d)
+                    i = (y - y01) * crop[1] + (x - x01)
+                    xj, yj = J % Wj - x02, J // Wj - y02
+                    if not (0 <= xj < crop[1] and 0 <= yj < crop[0]):
+                        continue
+                    j = yj * crop[1] + xj
+                    s = float(ca[i] @ cb[j])
+                    ok = s >= float((ca[i] @ cb.T).max()) - TAU and s >= float((cb[j] @ ca.T).max()) - TAU
+                    if ok:
+                        break
+            assert ok, (I, J)
+    print(f"{H}x{W}: tiles {len(crops)} pairs gpu {len(gi)} oracle {len(ref['i'])} "
+          f"coarse sharp {coarse_sharp} fine sharp {fine_sharp}")
+
+
+def test_c2f_rejects_bad_sizes(ddm):
+    import torch
+    x = torch.zeros(64, 48, 24, dtype=torch.float16, device="cuda")
+    with pytest.raises(ddm.DDMError):
+        ddm.c2f_match(x, x, crop=(65, 48))
+    y = torch.zeros(64, 48, 23, dtype=torch.float16, device="cuda")
+    with pytest.raises(ddm.DDMError):
+        ddm.c2f_match(y, y, crop=(32, 24))
