@@ -70,6 +70,7 @@ def _declare(lib):
     lib.ddm_c2f_match.restype = I
     lib.ddm_frm_set_mode.argtypes = [I]; lib.ddm_frm_set_mode.restype = I
     lib.ddm_frm_get_mode.argtypes = []; lib.ddm_frm_get_mode.restype = I
+    lib.ddm_frm_set_barrier_polls.argtypes = [I]; lib.ddm_frm_set_barrier_polls.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
     lib.ddm_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]; lib.ddm_profile_read.restype = I
     return lib
@@ -132,6 +133,12 @@ def frm_set_mode(mode: int):
 
 def frm_get_mode() -> int:
     return lib().ddm_frm_get_mode()
+
+
+def frm_set_barrier_polls(polls: int):
+    """Polls a grid-barrier wait of the loop mode makes before it gives up (0: the default).
+    A test aid: a tiny value makes loop-mode calls report failure instead of matches."""
+    _rc(lib().ddm_frm_set_barrier_polls(polls), "ddm_frm_set_barrier_polls")
 
 
 def profile_enable(mask: int):

@@ -505,6 +505,9 @@ void frm_dir_args(const FrmPlan &P, const void *m1q, const void *m1r, const void
     r->neg_out = f.l2 ? 1 : 0;
 }
 
+// Polls per grid-barrier wait of the loop kernel (a test aid lowers it to force the failure path).
+std::atomic<int> &loop_spin_limit() { static std::atomic<int> n{kSpinLimit}; return n; }
+
 // Half-steps [0, h_loop) run as one sweep and one update launch each, the
 // rest (all of them in the loop mode) in one cooperative loop kernel that
 // stops when no seed is active. The whole sequence can be captured into a graph.
@@ -562,7 +565,7 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
         frm_dir_args(P, m1, m1r, m2, m2r, part, 1, &fa.sw[1], &fa.rs[1]);
         fa.st = st; fa.B = P.B; fa.nhalf = P.nhalf; fa.k = P.k; fa.qblocks = P.qblocks;
         fa.nch[0] = P.nch2; fa.nch[1] = P.nch1;
-        fa.bar = ctl; fa.err = (int32_t *)(ctl + 32);
+        fa.bar = ctl; fa.err = (int32_t *)(ctl + 32); fa.spin_limit = loop_spin_limit().load();
         const long long sweep_tasks = (long long)P.B * P.qblocks * std::max(P.nch1, P.nch2);
         const long long upd_tasks = (long long)P.B * ((P.k + 15) / 16);
         for (int h = 0; h < std::min(h_loop, P.nhalf); ++h) {
@@ -594,7 +597,7 @@ struct C2fPlan {
     int kc, kf, nblk;
     FrmPlan pc, pf;           // coarse FRM (one pair) and fine FRM (one pair per tile)
     size_t o_c1, o_c2, o_cws, o_ci, o_cj, o_cs, o_cc, o_info, o_b1, o_b2, o_fws, o_fi, o_fj, o_fs, o_fc, o_owner,
-        o_mj, o_ms, o_bc, o_bo, total;
+        o_mj, o_ms, o_bc, o_bo, o_err, total;
     CropGeom geom() const {
         return CropGeom{H1, W1, H2, W2, CH, CW, ntx, nty, factor, Wc1, Wc2};
     }
@@ -637,6 +640,7 @@ int c2f_plan(int H1, int W1, int H2, int W2, int d, int dtype, int factor, int c
     const size_t n1 = (size_t)H1 * W1;
     p->o_owner = b.take(n1 * 4); p->o_mj = b.take(n1 * 4); p->o_ms = b.take(n1 * 4);
     p->o_bc = b.take((size_t)p->nblk * 4); p->o_bo = b.take((size_t)p->nblk * 4);
+    p->o_err = b.take(4);
     p->total = b.off;
     return DDM_OK;
 }
@@ -687,8 +691,12 @@ int c2f_run(const C2fPlan &P, const void *F1, const void *F2, int32_t *out_i, in
                        (const float *)fsc, (const int32_t *)fc, P.kf, g, (const int32_t *)info,
                        (const int32_t *)owner, mj, ms);
     DDM_CHECK_LAUNCH();
+    int32_t *err = (int32_t *)(w + P.o_err);
+    hipLaunchKernelGGL(c2f_status_kernel, dim3(1), dim3(256), 0, s, (const int32_t *)cc, (const int32_t *)fc,
+                       P.ntiles, err);
+    DDM_CHECK_LAUNCH();
     return compact_run(mj, ms, n1, n1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo), out_i, out_j,
-                       out_score, capacity, out_count, s);
+                       out_score, capacity, out_count, s, (const int32_t *)err);
 }
 
 // -------------------------------------------------------------- mutual plan
@@ -821,6 +829,12 @@ int ddm_frm_set_mode(int mode) {
 
 int ddm_frm_get_mode(void) { return frm_mode().load(); }
 
+int ddm_frm_set_barrier_polls(int polls) {
+    if (polls < 0) return DDM_ERR_INVALID;
+    loop_spin_limit().store(polls == 0 ? kSpinLimit : polls);
+    return DDM_OK;
+}
+
 int ddm_profile_enable(int mask) {
     if (mask < 0 || mask > 3) return DDM_ERR_INVALID;
     std::lock_guard<std::mutex> g(prof().mu);
@@ -933,7 +947,8 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)seed_state,
                           (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, (uint64_t)h_loop,
                           (uint64_t)(uintptr_t)O.starts, (uint64_t)(uint32_t)O.n_starts, tol_bits,
-                          (uint64_t)(uintptr_t)O.basin, (uint64_t)metric};
+                          (uint64_t)(uintptr_t)O.basin, (uint64_t)metric,
+                          (uint64_t)(h_loop == 0 ? loop_spin_limit().load() : 0)};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return frm_run(P, O, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts,
                        workspace, s, h_loop);
@@ -1011,7 +1026,8 @@ int ddm_c2f_match(const void *F1, int H1, int W1, const void *F2, int H2, int W2
                           (uint64_t)crop_w, (uint64_t)fine_stride, (uint64_t)fine_iter, (uint64_t)(uintptr_t)out_i,
                           (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)crop_info,
-                          (uint64_t)(uintptr_t)workspace, (uint64_t)loop};
+                          (uint64_t)(uintptr_t)workspace, (uint64_t)loop,
+                          (uint64_t)(loop ? loop_spin_limit().load() : 0)};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return c2f_run(P, F1, F2, out_i, out_j, out_score, capacity, out_count, crop_info, workspace, s, loop);
     });

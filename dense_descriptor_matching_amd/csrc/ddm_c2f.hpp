@@ -131,6 +131,15 @@ __global__ void __launch_bounds__(256) crop_write_kernel(const int32_t *fi, cons
     }
 }
 
+// flag = 1 when the coarse FRM or any tile's fine FRM reported failure (count -1).
+__global__ void __launch_bounds__(256) c2f_status_kernel(const int32_t *ccount, const int32_t *fcount, int ntiles,
+                                                         int32_t *flag) {
+    int bad = threadIdx.x == 0 && ccount[0] < 0;
+    for (int t = threadIdx.x; t < ntiles; t += 256) bad |= fcount[t] < 0;
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) *flag = bad;
+}
+
 __global__ void __launch_bounds__(256) c2f_clear_kernel(int32_t *owner, int32_t *match_j, int n) {
     for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
         owner[i] = 0x7fffffff;

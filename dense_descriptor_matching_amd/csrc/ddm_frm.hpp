@@ -26,6 +26,7 @@ struct FrmArgs {
     int nch[2];
     uint32_t *bar;        // loop kernel: barrier arrivals, zero at launch
     int32_t *err;         // loop kernel: set to 1 when a barrier wait ran past its bound
+    int spin_limit;       // loop kernel: polls per barrier wait before giving up
 };
 
 // Task t of a phase -> (pair, task within the pair), given the per-pair counts.
@@ -96,21 +97,21 @@ __global__ void __launch_bounds__(256) frm_update_kernel(FrmArgs a, int h) {
     frm_update_phase<DT, 256>(a, h, red);
 }
 
-constexpr int kSpinLimit = 1 << 20;   // polls per barrier wait (each one an uncached load + s_sleep): ~1 s
+constexpr int kSpinLimit = 1 << 20;   // default polls per barrier wait (each an uncached load + s_sleep): ~1 s
 
 // Grid-wide barrier on a monotonically increasing arrival counter: each
 // workgroup adds one arrival and waits for `target` (= barriers so far x
 // workgroups). Release/acquire at agent scope make the global writes before the
 // barrier visible to every workgroup after it. Returns false, uniformly over
 // the workgroup, if the wait timed out (then or at an earlier barrier).
-__device__ __forceinline__ bool grid_sync(uint32_t *bar, uint32_t target, int32_t *err, int *flag) {
+__device__ __forceinline__ bool grid_sync(uint32_t *bar, uint32_t target, int32_t *err, int spin_limit, int *flag) {
     __syncthreads();
     if (threadIdx.x == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int ok = 1, spins = 0;
         while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++spins > kSpinLimit) {
+            if (++spins > spin_limit) {
                 __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
                 break;
@@ -136,10 +137,10 @@ __global__ void __launch_bounds__(NW * 64) frm_loop_kernel(FrmArgs a, int h_begi
         if (!any) break;
         frm_sweep_phase<DT, NP, NKB, RQ, NW>(a, h, lds);
         target += gridDim.x;
-        if (!grid_sync(a.bar, target, a.err, &flag)) return;
+        if (!grid_sync(a.bar, target, a.err, a.spin_limit, &flag)) return;
         frm_update_phase<DT, NW * 64>(a, h, reinterpret_cast<uint64_t *>(lds));
         target += gridDim.x;
-        if (!grid_sync(a.bar, target, a.err, &flag)) return;
+        if (!grid_sync(a.bar, target, a.err, a.spin_limit, &flag)) return;
     }
 }
 

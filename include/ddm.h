@@ -182,6 +182,11 @@ int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
 typedef enum { DDM_FRM_PER_HALF_STEP = 0, DDM_FRM_LOOP = 1 } ddm_frm_mode;
 int ddm_frm_set_mode(int mode);
 int ddm_frm_get_mode(void);
+/* Test aid for the failure path of DDM_FRM_LOOP: the number of polls a grid-barrier wait makes
+ * before giving up (0 restores the default of 2^20, about 1 s). A tiny value makes the barriers
+ * time out on purpose; the kernel still ends and out_count reads -1. Process-wide; graph-cached
+ * calls keep the value they were recorded with. */
+int ddm_frm_set_barrier_polls(int polls);
 
 /* ----------------------------------------------------- coarse-to-fine ---
  * Matching of maps larger than the network's 512-px input ("MASt3R" note on cv-learn.com,
@@ -201,7 +206,8 @@ int ddm_frm_get_mode(void);
  * capacity >= min(H1*W1, tiles * ddm_seed_count(crop_h, crop_w, fine_stride)).
  *   crop_info  device int32[tiles][5] or NULL: x0_1, y0_1, x0_2, y0_2, coarse pairs in the tile.
  * Requires crop sizes within both maps, factor >= 1, d * element size a multiple of 4 bytes,
- * W2 + H2 < 16384. FRM calls inside follow ddm_frm_set_mode. */
+ * W2 + H2 < 16384. FRM calls inside follow ddm_frm_set_mode; out_count = -1 when one of them
+ * reported a failed synchronisation (as for ddm_frm_match). */
 size_t ddm_c2f_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype, int factor,
                                int coarse_stride, int coarse_iter, int crop_h, int crop_w,
                                int fine_stride, int fine_iter);

@@ -41,6 +41,12 @@ def test_frm_mode_switch(L):
     assert L.ddm_frm_set_mode(0) == 0 and L.ddm_frm_get_mode() == 0
 
 
+def test_barrier_polls_setter(L):
+    assert L.ddm_frm_set_barrier_polls(-1) == -1
+    assert L.ddm_frm_set_barrier_polls(3) == 0
+    assert L.ddm_frm_set_barrier_polls(0) == 0      # back to the default bound
+
+
 def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5):
         assert L.ddm_status_str(code)
