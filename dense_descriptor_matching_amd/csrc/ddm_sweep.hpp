@@ -118,27 +118,35 @@ struct SweepArgs {
     int nchunks;
     int sb_per_wg;               // query sub-blocks per workgroup
     int rowcap;                  // rows per chunk slice of rowpart (without split)
-    // Runtime split (used with a device query count): when the count leaves
-    // query blocks idle and the pair's busy workgroups fall short of `split`,
-    // each reference chunk is cut into s sub-chunks (whole index groups)
-    // handled by the idle blocks; partial slot chunk*s + sub.
-    int split;                   // workgroups per pair to aim for; 0 = off
+    // Runtime split (used with a device query count), aiming at `split` tasks
+    // per pair: when the count leaves query blocks idle and the pair's busy
+    // workgroups fall short of it, each reference chunk is cut into s
+    // sub-chunks (whole index groups) handled by the idle blocks, partial slot
+    // chunk*s + sub; when the count gives at least twice as many (chunk,
+    // sub-block) tasks, consecutive sub-blocks are grouped into one task so the
+    // staged chunk serves several of them.
+    int split;                   // tasks per pair to aim for; 0 = off
     int qblocks;                 // query blocks in the grid
     int split_rows;              // query rows per query block
 };
 
-// Geometry of the runtime split for nq queries: blocks with work (need),
-// sub-chunks per chunk (s) and rows per partial slot (rowcap). The sweep and
-// the resolve of one half-step evaluate it on the same count.
-struct SplitGeom { int need, s, rowcap; };
+// Geometry of the runtime split for nq queries: query tasks per chunk (need),
+// sub-chunks per chunk (s), rows per partial slot (rowcap) and sub-blocks per
+// query task (spw; 0 = the launch's sb_per_wg). The sweep and the resolve of
+// one half-step evaluate it on the same count.
+struct SplitGeom { int need, s, rowcap, spw; };
 __device__ __forceinline__ SplitGeom split_geom(int split, int nq, int rows, int qblocks, int groups_per_chunk,
                                                 int nchunks, int rowcap) {
-    if (!split) return SplitGeom{qblocks, 1, rowcap};
-    const int need = max(1, (nq + rows - 1) / rows);
-    const int busy = need * nchunks;
+    if (!split) return SplitGeom{qblocks, 1, rowcap, 0};
+    const int nsb = max(1, (nq + rows - 1) / rows);
+    const int busy = nsb * nchunks;
+    if (busy >= 2 * split) {
+        const int spw = min(nsb, busy / split);
+        return SplitGeom{(nsb + spw - 1) / spw, 1, nsb * rows, spw};
+    }
     const int want = (split + busy - 1) / busy;
-    const int s = max(1, min(want, min(qblocks / need, groups_per_chunk)));
-    return SplitGeom{need, s, need * rows};
+    const int s = max(1, min(want, min(qblocks / nsb, groups_per_chunk)));
+    return SplitGeom{nsb, s, nsb * rows, 1};
 }
 
 // Row-partial key: high word = order-preserving key of the row maximum, low
@@ -173,6 +181,208 @@ __device__ __forceinline__ uint32_t row16_min(uint32_t x) {
     return x;
 }
 
+// Queries of one sub-block against the staged chunk. Wave w takes the
+// sub-block's 16-row tiles w, w + NW, ..., RQ of them; rows past the query
+// count repeat the last valid row (no column maximum changes) and are not
+// written back.
+template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
+__device__ __forceinline__ void sweep_rows(const SweepArgs &p, const unsigned char *Q, const int32_t *qrows, int nq,
+                                           int sb_row0, int np, int TB, int nkb, int ngroups,
+                                           const int (&boff)[NKB], uint32_t gbase, uint64_t *rp, float *colmax_lds,
+                                           const unsigned char *lds) {
+    constexpr int G = group_tiles(DT);
+    using T = Tr<DT>;
+    using raw = typename T::raw;
+    constexpr int PS = T::PS, ESZ = T::ESZ;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    auto row_of = [&](int qt) { return sb_row0 + (wave + qt * NW) * 16; };
+
+    raw a[RQ][NKB];
+#pragma unroll
+    for (int qt = 0; qt < RQ; ++qt) {
+        int rr = min(row_of(qt) + c, nq - 1);
+        const int qrow = qrows ? qrows[rr] : rr;
+        const unsigned char *qp = Q + (long long)qrow * p.ld * ESZ;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int pc = kb * 4 + g;
+            a[qt][kb] = (pc < np) ? *reinterpret_cast<const raw *>(qp + pc * PS) : T::zero();
+        }
+    }
+
+    // Running row state lives in two register sets that swap roles every
+    // group, so no copies are needed between groups.
+    float bA[RQ][4], bB[RQ][4];
+    int gid[RQ][4];
+#pragma unroll
+    for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { bA[qt][r] = -INFINITY; gid[qt][r] = 0; }
+
+    // ---- per tile pair: B fragments from LDS, MFMAs, epilogue
+    auto load_pair = [&](int tile, raw (&b0)[NKB], raw (&b1)[NKB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            b0[kb] = *reinterpret_cast<const raw *>(lds + tile * TB + boff[kb]);
+            b1[kb] = *reinterpret_cast<const raw *>(lds + (tile + 1) * TB + boff[kb]);
+        }
+    };
+    auto mma_pair = [&](const raw (&b0)[NKB], const raw (&b1)[NKB], f32x4_t (&c0)[RQ],
+                        f32x4_t (&c1)[RQ]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qt = 0; qt < RQ; ++qt) {
+            c0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            c1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                if (NP > 0 || kb < nkb) {
+                    c0[qt] = T::mma(a[qt][kb], b0[kb], c0[qt]);
+                    c1[qt] = T::mma(a[qt][kb], b1[kb], c1[qt]);
+                }
+            }
+        }
+    };
+    // Row state: running maximum of each (row, slot) over the group's tiles,
+    // v_max3 consumes one score of each tile of the pair. Columns: in-lane
+    // maximum over the wave's rows, one LDS float-max per tile (the four
+    // lanes of a column, one per row group, meet in LDS).
+    auto epi_pair = [&](const f32x4_t (&c0)[RQ], const f32x4_t (&c1)[RQ], int tile, bool first,
+                        float (&bin)[RQ][4], float (&bout)[RQ][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                bout[qt][r] = fmaxf(fmaxf(first ? bin[qt][r] : bout[qt][r], c0[qt][r]), c1[qt][r]);
+        if constexpr (COLMAX) {
+            float m0 = fmaxf(c0[0][0], c0[0][1]);
+            float m1 = fmaxf(c1[0][0], c1[0][1]);
+            m0 = fmaxf(fmaxf(m0, c0[0][2]), c0[0][3]);
+            m1 = fmaxf(fmaxf(m1, c1[0][2]), c1[0][3]);
+#pragma unroll
+            for (int qt = 1; qt < RQ; ++qt) {
+                m0 = fmaxf(fmaxf(m0, c0[qt][0]), c0[qt][1]);
+                m0 = fmaxf(fmaxf(m0, c0[qt][2]), c0[qt][3]);
+                m1 = fmaxf(fmaxf(m1, c1[qt][0]), c1[qt][1]);
+                m1 = fmaxf(fmaxf(m1, c1[qt][2]), c1[qt][3]);
+            }
+            float *cm = colmax_lds + tile * TILE + c;
+            __hip_atomic_fetch_max(cm, m0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_max(cm + TILE, m1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    };
+    auto mark = [&](int grp, float (&bin)[RQ][4], float (&bout)[RQ][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gid[qt][r] = (bout[qt][r] > bin[qt][r]) ? grp : gid[qt][r];
+    };
+
+    if constexpr (DT == DT_F32) {
+        // fp32 maps (narrow K blocks, small maps): plain loop, tile loop kept rolled
+        for (int grp = 0; grp < ngroups; ++grp) {
+            for (int tp = 0; tp < G; tp += 2) {
+                raw b0[NKB], b1[NKB];
+                f32x4_t c0[RQ], c1[RQ];
+                load_pair(grp * G + tp, b0, b1);
+                mma_pair(b0, b1, c0, c1);
+                epi_pair(c0, c1, grp * G + tp, tp == 0, bA, bB);
+            }
+            mark(grp, bA, bB);
+#pragma unroll
+            for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bA[qt][r] = bB[qt][r];
+        }
+    } else {
+        // Software pipeline over tile pairs: the next pair's B fragments and
+        // MFMAs are issued before the current pair's epilogue, so the matrix
+        // cores work while the VALU reduces. Two accumulator sets alternate;
+        // the row state alternates between bA and bB every group.
+        const int last_tile = ngroups * G - 2;
+        raw b0[NKB], b1[NKB];
+        f32x4_t xA0[RQ], xA1[RQ], xB0[RQ], xB1[RQ];
+        load_pair(0, b0, b1);
+        mma_pair(b0, b1, xA0, xA1);
+        int grp = 0;
+        for (; grp + 1 < ngroups; grp += 2) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                const int tile = grp * G + 2 * q;
+                const int ntile = min(tile + 2, last_tile);
+                const bool second = q >= G / 2;
+                load_pair(ntile, b0, b1);
+                if (q % 2 == 0) {
+                    mma_pair(b0, b1, xB0, xB1);
+                    if (!second) epi_pair(xA0, xA1, tile, q == 0, bA, bB);
+                    else epi_pair(xA0, xA1, tile, q == G / 2, bB, bA);
+                } else {
+                    mma_pair(b0, b1, xA0, xA1);
+                    if (!second) epi_pair(xB0, xB1, tile, false, bA, bB);
+                    else epi_pair(xB0, xB1, tile, false, bB, bA);
+                }
+                if (q == G / 2 - 1) mark(grp, bA, bB);
+                if (q == G - 1) mark(grp + 1, bB, bA);
+            }
+        }
+        if (grp < ngroups) {
+#pragma unroll
+            for (int q = 0; q < G / 2; ++q) {
+                const int tile = grp * G + 2 * q;
+                const int ntile = min(tile + 2, last_tile);
+                load_pair(ntile, b0, b1);
+                if (q % 2 == 0) {
+                    mma_pair(b0, b1, xB0, xB1);
+                    epi_pair(xA0, xA1, tile, q == 0, bA, bB);
+                } else {
+                    mma_pair(b0, b1, xA0, xA1);
+                    epi_pair(xB0, xB1, tile, false, bA, bB);
+                }
+            }
+            mark(grp, bA, bB);
+#pragma unroll
+            for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bA[qt][r] = bB[qt][r];
+        }
+    }
+
+    // ---- row flush: max over the 16 slots of each row, lowest (group, slot) among equals
+#pragma unroll
+    for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float bv = bA[qt][r];
+            const float m = row16_max(bv);
+            const uint32_t id = ((gbase + (uint32_t)gid[qt][r]) << 4) | (uint32_t)c;
+            const uint32_t cand = row16_min(bv == m ? id : 0xffffffffu);
+            const int row = row_of(qt) + 4 * g + r;
+            if (c == 0 && row < nq) rp[row] = row_key(m, cand);
+        }
+}
+
+// sweep_rows with as few query tiles per wave as the sub-block needs (tpw = 16-row
+// tiles of the busiest wave): a half-step with few active queries costs a
+// fraction of a full one. The fused column-maximum sweep always takes RQ.
+template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
+__device__ __forceinline__ void sweep_rows_fit(int tpw, const SweepArgs &p, const unsigned char *Q,
+                                               const int32_t *qrows, int nq, int sb_row0, int np, int TB, int nkb,
+                                               int ngroups, const int (&boff)[NKB], uint32_t gbase, uint64_t *rp,
+                                               float *colmax_lds, const unsigned char *lds) {
+#define DDM_SWEEP_ROWS(RQV) \
+    sweep_rows<DT, NP, NKB, RQV, NW, COLMAX>(p, Q, qrows, nq, sb_row0, np, TB, nkb, ngroups, boff, gbase, rp, \
+                                             colmax_lds, lds)
+    if constexpr (COLMAX) {
+        DDM_SWEEP_ROWS(RQ);
+    } else {
+        if (tpw <= 1) { DDM_SWEEP_ROWS(1); return; }
+        if constexpr (RQ > 2) { if (tpw <= 2) { DDM_SWEEP_ROWS(2); return; } }
+        if constexpr (RQ > 3) { if (tpw <= 3) { DDM_SWEEP_ROWS(3); return; } }
+        if constexpr (RQ > 1) DDM_SWEEP_ROWS(RQ);
+    }
+#undef DDM_SWEEP_ROWS
+}
+
 // NP = pieces (of E elements) per stored row; 0 = runtime (fp32 path).
 // NKB = 32-wide (fp16/bf16) or 4-wide (fp32) K blocks.
 // One workgroup task: reference chunk chunk_id of pair `pair` against query
@@ -196,10 +406,11 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
         sub = qblk / sg.need;
         if (sub >= sg.s) return;
     }
+    const int spw = sg.spw > 0 ? sg.spw : p.sb_per_wg;
     const int n_sb = (nq + SB_ROWS - 1) / SB_ROWS;
-    const int sb_first = qb * p.sb_per_wg;
+    const int sb_first = qb * spw;
     if (sb_first >= n_sb) return;
-    const int sb_last = min(sb_first + p.sb_per_wg, n_sb);
+    const int sb_last = min(sb_first + spw, n_sb);
     uint64_t *rp = p.rowpart + pair * p.rowpart_bs + (long long)(chunk_id * sg.s + sub) * sg.rowcap;
 
     const unsigned char *Q = p.Q + pair * p.q_bs;
@@ -221,18 +432,33 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
     const int ngroups = (nvalid + GROUP - 1) / GROUP;
     const int nslots = ngroups * GROUP;
 
-    // ---- stage the chunk in LDS: slot c of tile t of group q <- reference q*GROUP + G*c + t
-    for (int qq = tid; qq < nslots * np; qq += NW * 64) {
-        const int r = qq / np, pc = qq - r * np;
-        raw v;
-        if (r < nvalid)
-            v = *reinterpret_cast<const raw *>(R + ((long long)(r0 + r) * p.ld + pc * E) * ESZ);
-        else
-            v = T::nan_piece();
-        const int grp = r / GROUP, w = r % GROUP;
-        const int tile = grp * G + (w % G);
-        const int c = w / G;
-        *reinterpret_cast<raw *>(lds + tile * TB + pc * 16 * PS + c * PS) = v;
+    // ---- stage the chunk in LDS: slot c of tile t of group q <- reference q*GROUP + G*c + t.
+    // Each thread issues SU loads before storing any of them, so the staging
+    // waits for memory once per SU pieces rather than once per piece.
+    {
+        constexpr int SU = 8;
+        const int total = nslots * np;
+        for (int base = 0; base < total; base += SU * NW * 64) {
+            raw v[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int qq = base + u * NW * 64 + tid;
+                const int r = qq / np, pc = qq - r * np;
+                v[u] = T::nan_piece();
+                if (qq < total && r < nvalid)
+                    v[u] = *reinterpret_cast<const raw *>(R + ((long long)(r0 + r) * p.ld + pc * E) * ESZ);
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int qq = base + u * NW * 64 + tid;
+                if (qq >= total) break;
+                const int r = qq / np, pc = qq - r * np;
+                const int grp = r / GROUP, w = r % GROUP;
+                const int tile = grp * G + (w % G);
+                const int c = w / G;
+                *reinterpret_cast<raw *>(lds + tile * TB + pc * 16 * PS + c * PS) = v[u];
+            }
+        }
     }
     float *colmax_lds = reinterpret_cast<float *>(lds + (size_t)(p.chunk / TILE) * TB);
     if constexpr (COLMAX) {
@@ -250,170 +476,11 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
     const uint32_t gbase = (uint32_t)(r0 / GROUP);
 
     for (int sb = sb_first; sb < sb_last; ++sb) {
-        const int row0 = sb * SB_ROWS + wave * RQ * 16;
-        if (row0 >= nq) break;
-
-        raw a[RQ][NKB];
-#pragma unroll
-        for (int qt = 0; qt < RQ; ++qt) {
-            int rr = min(row0 + qt * 16 + c, nq - 1);
-            const int qrow = qrows ? qrows[rr] : rr;
-            const unsigned char *qp = Q + (long long)qrow * p.ld * ESZ;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const int pc = kb * 4 + g;
-                a[qt][kb] = (pc < np) ? *reinterpret_cast<const raw *>(qp + pc * PS) : T::zero();
-            }
-        }
-
-        // Running row state lives in two register sets that swap roles every
-        // group, so no copies are needed between groups.
-        float bA[RQ][4], bB[RQ][4];
-        int gid[RQ][4];
-#pragma unroll
-        for (int qt = 0; qt < RQ; ++qt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) { bA[qt][r] = -INFINITY; gid[qt][r] = 0; }
-
-        // ---- per tile pair: B fragments from LDS, MFMAs, epilogue
-        auto load_pair = [&](int tile, raw (&b0)[NKB], raw (&b1)[NKB]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                b0[kb] = *reinterpret_cast<const raw *>(lds + tile * TB + boff[kb]);
-                b1[kb] = *reinterpret_cast<const raw *>(lds + (tile + 1) * TB + boff[kb]);
-            }
-        };
-        auto mma_pair = [&](const raw (&b0)[NKB], const raw (&b1)[NKB], f32x4_t (&c0)[RQ],
-                            f32x4_t (&c1)[RQ]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int qt = 0; qt < RQ; ++qt) {
-                c0[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                c1[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    if (NP > 0 || kb < nkb) {
-                        c0[qt] = T::mma(a[qt][kb], b0[kb], c0[qt]);
-                        c1[qt] = T::mma(a[qt][kb], b1[kb], c1[qt]);
-                    }
-                }
-            }
-        };
-        // Row state: running maximum of each (row, slot) over the group's tiles,
-        // v_max3 consumes one score of each tile of the pair. Columns: in-lane
-        // maximum over the wave's rows, one LDS float-max per tile (the four
-        // lanes of a column, one per row group, meet in LDS).
-        auto epi_pair = [&](const f32x4_t (&c0)[RQ], const f32x4_t (&c1)[RQ], int tile, bool first,
-                            float (&bin)[RQ][4], float (&bout)[RQ][4]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int qt = 0; qt < RQ; ++qt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    bout[qt][r] = fmaxf(fmaxf(first ? bin[qt][r] : bout[qt][r], c0[qt][r]), c1[qt][r]);
-            if constexpr (COLMAX) {
-                float m0 = fmaxf(c0[0][0], c0[0][1]);
-                float m1 = fmaxf(c1[0][0], c1[0][1]);
-                m0 = fmaxf(fmaxf(m0, c0[0][2]), c0[0][3]);
-                m1 = fmaxf(fmaxf(m1, c1[0][2]), c1[0][3]);
-#pragma unroll
-                for (int qt = 1; qt < RQ; ++qt) {
-                    m0 = fmaxf(fmaxf(m0, c0[qt][0]), c0[qt][1]);
-                    m0 = fmaxf(fmaxf(m0, c0[qt][2]), c0[qt][3]);
-                    m1 = fmaxf(fmaxf(m1, c1[qt][0]), c1[qt][1]);
-                    m1 = fmaxf(fmaxf(m1, c1[qt][2]), c1[qt][3]);
-                }
-                float *cm = colmax_lds + tile * TILE + c;
-                __hip_atomic_fetch_max(cm, m0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                __hip_atomic_fetch_max(cm + TILE, m1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-        };
-        auto mark = [&](int grp, float (&bin)[RQ][4], float (&bout)[RQ][4]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int qt = 0; qt < RQ; ++qt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gid[qt][r] = (bout[qt][r] > bin[qt][r]) ? grp : gid[qt][r];
-        };
-
-        if constexpr (DT == DT_F32) {
-            // fp32 maps (narrow K blocks, small maps): plain loop, tile loop kept rolled
-            for (int grp = 0; grp < ngroups; ++grp) {
-                for (int tp = 0; tp < G; tp += 2) {
-                    raw b0[NKB], b1[NKB];
-                    f32x4_t c0[RQ], c1[RQ];
-                    load_pair(grp * G + tp, b0, b1);
-                    mma_pair(b0, b1, c0, c1);
-                    epi_pair(c0, c1, grp * G + tp, tp == 0, bA, bB);
-                }
-                mark(grp, bA, bB);
-#pragma unroll
-                for (int qt = 0; qt < RQ; ++qt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) bA[qt][r] = bB[qt][r];
-            }
-        } else {
-            // Software pipeline over tile pairs: the next pair's B fragments and
-            // MFMAs are issued before the current pair's epilogue, so the matrix
-            // cores work while the VALU reduces. Two accumulator sets alternate;
-            // the row state alternates between bA and bB every group.
-            const int last_tile = ngroups * G - 2;
-            raw b0[NKB], b1[NKB];
-            f32x4_t xA0[RQ], xA1[RQ], xB0[RQ], xB1[RQ];
-            load_pair(0, b0, b1);
-            mma_pair(b0, b1, xA0, xA1);
-            int grp = 0;
-            for (; grp + 1 < ngroups; grp += 2) {
-#pragma unroll
-                for (int q = 0; q < G; ++q) {
-                    const int tile = grp * G + 2 * q;
-                    const int ntile = min(tile + 2, last_tile);
-                    const bool second = q >= G / 2;
-                    load_pair(ntile, b0, b1);
-                    if (q % 2 == 0) {
-                        mma_pair(b0, b1, xB0, xB1);
-                        if (!second) epi_pair(xA0, xA1, tile, q == 0, bA, bB);
-                        else epi_pair(xA0, xA1, tile, q == G / 2, bB, bA);
-                    } else {
-                        mma_pair(b0, b1, xA0, xA1);
-                        if (!second) epi_pair(xB0, xB1, tile, false, bA, bB);
-                        else epi_pair(xB0, xB1, tile, false, bB, bA);
-                    }
-                    if (q == G / 2 - 1) mark(grp, bA, bB);
-                    if (q == G - 1) mark(grp + 1, bB, bA);
-                }
-            }
-            if (grp < ngroups) {
-#pragma unroll
-                for (int q = 0; q < G / 2; ++q) {
-                    const int tile = grp * G + 2 * q;
-                    const int ntile = min(tile + 2, last_tile);
-                    load_pair(ntile, b0, b1);
-                    if (q % 2 == 0) {
-                        mma_pair(b0, b1, xB0, xB1);
-                        epi_pair(xA0, xA1, tile, q == 0, bA, bB);
-                    } else {
-                        mma_pair(b0, b1, xA0, xA1);
-                        epi_pair(xB0, xB1, tile, false, bA, bB);
-                    }
-                }
-                mark(grp, bA, bB);
-#pragma unroll
-                for (int qt = 0; qt < RQ; ++qt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) bA[qt][r] = bB[qt][r];
-            }
-        }
-
-        // ---- row flush: max over the 16 slots of each row, lowest (group, slot) among equals
-#pragma unroll
-        for (int qt = 0; qt < RQ; ++qt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float bv = bA[qt][r];
-                const float m = row16_max(bv);
-                const uint32_t id = ((gbase + (uint32_t)gid[qt][r]) << 4) | (uint32_t)c;
-                const uint32_t cand = row16_min(bv == m ? id : 0xffffffffu);
-                const int row = row0 + qt * 16 + 4 * g + r;
-                if (c == 0 && row < nq) rp[row] = row_key(m, cand);
-            }
+        const int sb_row0 = sb * SB_ROWS;
+        const int tiles = (min(SB_ROWS, nq - sb_row0) + 15) / 16;     // 16-row tiles holding queries
+        if (wave >= tiles) break;
+        sweep_rows_fit<DT, NP, NKB, RQ, NW, COLMAX>((tiles + NW - 1) / NW, p, Q, qrows, nq, sb_row0, np, TB, nkb,
+                                                    ngroups, boff, gbase, rp, colmax_lds, lds);
     }
 
     if constexpr (COLMAX) {
