@@ -286,16 +286,20 @@ __global__ void __launch_bounds__(256) frm_seeds_from_starts_kernel(FrmState st,
 
 // One half-step's update for query block blk of pair `pair`: resolve each
 // active query, apply the cycle test and append the seeds that stay active to
-// the next list (wave ballot + one atomic per wave; list order does not affect
-// any result).
+// the next list. The block's survivors take one atomic on the pair's next
+// count (one per block rather than per wave: the count is a single contended
+// address); list order does not affect any result.
 template <int DT, int QB, int NT>
 __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmState &st, int h, int backward,
                                                 int iter, int pair, int blk, uint64_t *red) {
+    static_assert(QB <= 64, "survivors of a block are gathered by one wave");
+    __shared__ int keep_seed[QB], keep_j[QB];
     const int cur = h & 1, nxt = cur ^ 1;
     const long long ko = pair * st.k_bs;
     int32_t *counts = st.counts + pair * st.cnt_bs;
     const int nq = counts[h];
-    const int lane = threadIdx.x & 63;
+    const int x0 = blk * QB;
+    if (x0 >= nq) return;
     const unsigned char *Q = a.Q + pair * a.q_bs;
     const SplitGeom sg = split_geom(a.split, nq, a.split_rows, a.qblocks, a.chunk_groups, a.nchunks, a.rowcap);
     resolve_block<DT, QB, NT>(
@@ -303,10 +307,11 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
         a.ld, a.d,
         [&](int x) { return Q + (long long)st.qrows[cur][ko + x] * a.ld * Tr<DT>::ESZ; },
         [&](bool valid, int x, int j, float s, int sub) {
-            bool keep = false;
-            int seed = 0;
-            if (valid && sub == 0) {
+            if (sub != 0) return;
+            int seed = -1;
+            if (valid) {
                 seed = st.act[cur][ko + x];
+                bool keep;
                 if (!backward) {
                     keep = st.basin != nullptr || j != st.v[ko + seed];    // no forward test in the basin variant
                     st.v[ko + seed] = j;
@@ -319,21 +324,32 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
                     st.uiter[ko + seed] = iter;
                     if (st.basin) st.basin[pair * st.n1_bs + from] = j;
                 }
-                if (!keep) st.conv[ko + seed] = iter;
-            }
-            const uint64_t ball = __ballot(keep);
-            const int n = __popcll(ball);
-            if (n > 0) {
-                int base = 0;
-                if (lane == 0) base = atomicAdd(counts + h + 1, n);
-                base = __shfl(base, 0);
-                if (keep) {
-                    const int pos = base + __popcll(ball & ((1ull << lane) - 1ull));
-                    st.act[nxt][ko + pos] = seed;
-                    st.qrows[nxt][ko + pos] = j;
+                if (!keep) {
+                    st.conv[ko + seed] = iter;
+                    seed = -1;
                 }
             }
+            keep_seed[x - x0] = seed;
+            keep_j[x - x0] = j;
         });
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const bool in = lane < QB && x0 + lane < nq;
+        const int seed = in ? keep_seed[lane] : -1;
+        const uint64_t ball = __ballot(seed >= 0);
+        const int n = __popcll(ball);
+        if (n > 0) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(counts + h + 1, n);
+            base = __shfl(base, 0);
+            if (seed >= 0) {
+                const int pos = base + __popcll(ball & ((1ull << lane) - 1ull));
+                st.act[nxt][ko + pos] = seed;
+                st.qrows[nxt][ko + pos] = keep_j[lane];
+            }
+        }
+    }
 }
 
 // Converged seeds -> dense match array indexed by image-1 pixel (every seed
