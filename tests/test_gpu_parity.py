@@ -30,7 +30,10 @@ def dec(a, dtype):
 # ------------------------------------------------------------------ NN unit
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16, synth.F32])
 @pytest.mark.parametrize("M,N,d", [(1, 1, 24), (5, 300, 24), (37, 1000, 8), (513, 4099, 24), (700, 9000, 64),
-                                   (64, 2000, 3), (130, 5000, 100), (40, 3000, 128), (17, 777, 32)])
+                                   (64, 2000, 3), (130, 5000, 100), (40, 3000, 128), (17, 777, 32),
+                                   # query tiles per wave 3 (and 6 then 2 over two sub-blocks): every tile-count
+                                   # variant of the sweep loop, at K blocks 1, 2 and 4
+                                   (300, 2500, 24), (1000, 3000, 64), (333, 1500, 128)])
 def test_nn_matches_oracle(ddm, dtype, M, N, d):
     Q = synth.gaussian_rows(M, d, dtype, 1000 + M)
     R = synth.gaussian_rows(N, d, dtype, 2000 + N)
