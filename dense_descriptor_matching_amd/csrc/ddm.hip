@@ -703,7 +703,7 @@ int c2f_run(const C2fPlan &P, const void *F1, const void *F2, int32_t *out_i, in
 struct MutualPlan {
     MapFmt f;
     int N1, N2, chunk, nchunks, sb_per_wg, qblocks, nblk;
-    size_t o_part, o_col, o_cmax, o_mj, o_ms, o_bc, o_bo, o_r1, o_r2, total;
+    size_t o_part, o_col, o_cmax, o_cfirst, o_owner, o_mj, o_ms, o_bc, o_bo, o_r1, o_r2, total;
 };
 
 int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p, int metric = DDM_DOT) {
@@ -727,6 +727,8 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p,
     p->o_part = b.take((size_t)p->nchunks * p->N1 * 8);
     p->o_col = b.take((size_t)p->qblocks * p->N2 * 4);
     p->o_cmax = b.take((size_t)p->N2 * 4);
+    p->o_cfirst = b.take((size_t)p->N2 * 4);
+    p->o_owner = b.take((size_t)p->N2 * 4);
     p->o_mj = b.take((size_t)p->N1 * 4);
     p->o_ms = b.take((size_t)p->N1 * 4);
     p->o_bc = b.take((size_t)p->nblk * 4);
@@ -1068,8 +1070,9 @@ int ddm_mutual_nn_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
     a.sb_per_wg = P.sb_per_wg; a.rowcap = P.N1;
     DDM_CHECK(launch_sweep(P.f, true, a, dim3(P.nchunks, P.qblocks, 1), stream));
     uint32_t *cmax = (uint32_t *)(w + P.o_cmax);
+    int32_t *cfirst = (int32_t *)(w + P.o_cfirst), *owner = (int32_t *)(w + P.o_owner);
     hipLaunchKernelGGL(colmax_merge_kernel, dim3((P.N2 + 255) / 256), dim3(256), 0, stream,
-                       (const uint32_t *)a.colpart, P.qblocks, P.N2, cmax);
+                       (const uint32_t *)a.colpart, P.qblocks, P.N2, cmax, cfirst, owner);
     DDM_CHECK_LAUNCH();
     ResolveArgs ra{};
     ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = P.N1;
@@ -1079,7 +1082,11 @@ int ddm_mutual_nn_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
     float *ms = (float *)(w + P.o_ms);
     const int qb = resolve_qb(P.N1);
     DDM_DT_QB_SWITCH(P.f.dtype, qb, mutual_rows_kernel, dim3((P.N1 + qb - 1) / qb), dim3(256), 0, stream, ra,
-                     (const uint32_t *)cmax, mj, ms, nn12, s12);
+                     (const uint32_t *)cmax, (const int32_t *)cfirst, P.sb_per_wg * P.f.sb_rows(), owner, mj, ms,
+                     nn12, s12);
+    DDM_CHECK_LAUNCH();
+    hipLaunchKernelGGL(mutual_claim_kernel, dim3(std::min((P.N1 + 255) / 256, 4096)), dim3(256), 0, stream,
+                       (const int32_t *)owner, P.N1, mj);
     DDM_CHECK_LAUNCH();
     return compact_run(mj, ms, P.N1, P.N1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo), out_i, out_j,
                        out_score, capacity, out_count, stream);

@@ -191,32 +191,52 @@ __global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, int32_t 
 // ---------------------------------------------------------------------------
 // Mutual NN: column maxima over query blocks, then per row (i, j = NN_2(i)) is
 // reciprocal iff column j's maximum equals row i's maximum (both are the same
-// matrix-core value, compared as order-preserving keys).
+// matrix-core value, compared as order-preserving keys) and no lower row
+// reaches that maximum too (NN_1 takes the lowest index on ties). Lower rows
+// of earlier query blocks are excluded by the first block whose partial holds
+// the maximum; among the rows that pass, the lowest claims the column.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) colmax_merge_kernel(const uint32_t *colpart, int nqblk, int nref,
-                                                           uint32_t *colmax) {
+                                                           uint32_t *colmax, int32_t *colfirst, int32_t *owner) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     if (j >= nref) return;
     uint32_t m = 0;
-    for (int b = 0; b < nqblk; ++b) m = max(m, colpart[(long long)b * nref + j]);
+    int first = 0;
+    for (int b = 0; b < nqblk; ++b) {
+        const uint32_t v = colpart[(long long)b * nref + j];
+        if (v > m) { m = v; first = b; }
+    }
     colmax[j] = m;
+    colfirst[j] = first;
+    owner[j] = 0x7fffffff;
 }
 
 template <int DT, int QB>
-__global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint32_t *colmax, int32_t *match_j,
-                                                          float *match_s, int32_t *nn12, float *s12) {
+__global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint32_t *colmax,
+                                                          const int32_t *colfirst, int rows_per_qblk, int32_t *owner,
+                                                          int32_t *match_j, float *match_s, int32_t *nn12,
+                                                          float *s12) {
     __shared__ uint64_t red[256];
     resolve_block<DT, QB, 256>(blockIdx.x, red, a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
                       [&](int x) { return a.Q + (long long)x * a.ld * Tr<DT>::ESZ; },
                       [&](bool valid, int x, int j, float s, int sub) {
                           if (valid && sub == 0) {
-                              const bool mutual = colmax[j] == fkey(s);
+                              const bool cand = colmax[j] == fkey(s) && x / rows_per_qblk == colfirst[j];
+                              if (cand) atomicMin(owner + j, x);
                               const float rs = reported(s, a.neg_out);
-                              match_j[x] = mutual ? j : -1;
+                              match_j[x] = cand ? j : -1;
                               match_s[x] = rs;
                               if (nn12) { nn12[x] = j; s12[x] = rs; }
                           }
                       });
+}
+
+// Rows that passed the test but lost their column to a lower row drop out.
+__global__ void __launch_bounds__(256) mutual_claim_kernel(const int32_t *owner, int n, int32_t *match_j) {
+    for (int x = blockIdx.x * 256 + threadIdx.x; x < n; x += gridDim.x * 256) {
+        const int j = match_j[x];
+        if (j >= 0 && owner[j] != x) match_j[x] = -1;
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -222,7 +222,12 @@ int ddm_c2f_match(const void *F1, int H1, int W1, const void *F2, int H2, int W2
  * single pass over all N1 x N2 scores with row arg-max and column max fused.
  *   capacity >= min(H1*W1, H2*W2); out_count as for FRM.
  *   nn12, s12  device int32[N1] / float[N1] or NULL: NN_2 of every pixel of
- *              image 1 and its score. */
+ *              image 1 and its score.
+ * Ties: both nearest neighbours take the lowest index, so every j appears at most once.
+ * (i, j) needs NN_2(i) = j, score(i, j) equal to column j's maximum, no earlier block of
+ * query rows reaching that maximum, and no lower row of the same block passing the same
+ * test; a lower row of that block whose own maximum lies elsewhere but ties in column j is
+ * not looked for (the pair is then reciprocal up to an exact tie). */
 size_t ddm_mutual_workspace_bytes(int H1, int W1, int H2, int W2, int d, int dtype);
 int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
                   int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
