@@ -189,6 +189,26 @@ def random_map(H: int, W: int, d: int, dtype: int, seed: int) -> np.ndarray:
     return cast_stored(_unit(rng.standard_normal((H, W, d))), dtype)
 
 
+def large_shift_pair(H: int, W: int, d: int, dtype: int, seed: int, shift) -> Pair:
+    """A large noise-free shifted pair built in float32 to bound host memory: D1 unit
+    Gaussian; D2(x, y) = D1(x + dx, y + dy) with the same stored bits, fresh unit rows
+    where that pixel is outside image 1. Used for property checks at sizes the oracle
+    cannot sweep (the shift fixes every reciprocal pair)."""
+    dx, dy = shift
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((H, W, d), dtype=np.float32)
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    D1 = cast_stored(x, dtype)
+    del x
+    fresh = rng.standard_normal((H, W, d), dtype=np.float32)
+    fresh /= np.linalg.norm(fresh, axis=-1, keepdims=True)
+    D2 = cast_stored(fresh, dtype)
+    del fresh
+    ys, xs = slice(max(0, -dy), min(H, H - dy)), slice(max(0, -dx), min(W, W - dx))
+    D2[ys, xs] = D1[max(0, dy):min(H, H + dy), max(0, dx):min(W, W + dx)]
+    return Pair(D1, D2, dtype, name=f"large_shift_{H}x{W}x{d}", meta={"shift": (dx, dy)})
+
+
 def gaussian_rows(n: int, d: int, dtype: int, seed: int, unit: bool = True) -> np.ndarray:
     """n descriptor rows [n, d] in stored form (NN unit cases with arbitrary n)."""
     rng = np.random.Generator(np.random.PCG64(seed))
