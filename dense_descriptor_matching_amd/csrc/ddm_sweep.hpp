@@ -8,10 +8,13 @@
 // variant produces in the same pass.
 //
 // Work decomposition
-//   grid.x  = reference chunk (CHUNK rows, a multiple of 256), staged once in LDS
+//   grid.x  = reference chunk (whole index groups: 512 references, 128 for fp32),
+//             staged once in LDS
 //   grid.y  = query block (sb_per_wg sub-blocks of NW*RQ*16 rows)
 //   grid.z  = independent pair (batched calls)
-//   Each wave keeps RQ query tiles of 16 rows resident in VGPRs as MFMA A
+//   (The FRM kernels enumerate the same tasks from device counts instead.)
+//   In a sub-block, wave w keeps the 16-row query tiles w, w + NW, ... (RQ of
+//   them, fewer when the sub-block is short) resident in VGPRs as MFMA A
 //   operands and streams the chunk's 16-row reference tiles from LDS as B
 //   operands with v_mfma_f32_16x16x32_{f16,bf16} (v_mfma_f32_16x16x4_f32 for
 //   fp32 maps), K padded to 32 with zeros in A only.
