@@ -765,7 +765,7 @@ using GraphKey = std::array<uint64_t, 28>;
 struct GraphCache {
     std::mutex mu;
     std::list<std::pair<GraphKey, hipGraphExec_t>> lru;
-    hipStream_t cap = nullptr;
+    std::vector<hipStream_t> cap;     // per device: private capture stream (default priority)
     static constexpr size_t kMax = 8;
 };
 GraphCache &graphs() { static GraphCache g; return g; }
@@ -783,11 +783,14 @@ int run_graphed(const GraphKey &key, hipStream_t stream, Enqueue enqueue) {
             return hipGraphLaunch(G.lru.front().second, stream) == hipSuccess ? DDM_OK : DDM_ERR_HIP;
         }
     }
-    if (!G.cap && hipStreamCreateWithFlags(&G.cap, hipStreamNonBlocking) != hipSuccess) return DDM_ERR_HIP;
-    if (hipStreamBeginCapture(G.cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return DDM_ERR_HIP;
-    const int rc = enqueue(G.cap);
+    const int dev = (int)key[0];
+    if ((int)G.cap.size() <= dev) G.cap.resize(dev + 1, nullptr);
+    hipStream_t &cap = G.cap[dev];
+    if (!cap && hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) return DDM_ERR_HIP;
+    if (hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return DDM_ERR_HIP;
+    const int rc = enqueue(cap);
     hipGraph_t graph = nullptr;
-    const hipError_t ec = hipStreamEndCapture(G.cap, &graph);
+    const hipError_t ec = hipStreamEndCapture(cap, &graph);
     if (rc != DDM_OK || ec != hipSuccess) {
         if (graph) (void)hipGraphDestroy(graph);
         return rc != DDM_OK ? rc : DDM_ERR_HIP;
