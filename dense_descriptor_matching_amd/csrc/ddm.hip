@@ -354,7 +354,7 @@ int maybe_repack(const MapFmt &f, const void *src, long long rows, void *dst, hi
 struct NnPlan {
     MapFmt f;
     int NQ, M, N, chunk, nchunks, qblocks;
-    size_t o_part, o_rq, o_rr, total;
+    size_t o_part, o_rq, o_rr, o_rows, total;
 };
 
 int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p, int metric = DDM_DOT) {
@@ -373,6 +373,7 @@ int nn_plan(int NQ, int M, int N, int d, int dtype, NnPlan *p, int metric = DDM_
     p->o_part = b.take((size_t)p->nchunks * M * 8);
     p->o_rq = p->f.repack ? b.take((size_t)NQ * p->f.ld * p->f.esz) : 0;
     p->o_rr = p->f.repack ? b.take((size_t)N * p->f.ld * p->f.esz) : 0;
+    p->o_rows = b.take((size_t)M * 4);
     p->total = b.off;
     return DDM_OK;
 }
@@ -895,19 +896,27 @@ int ddm_nn_ex(const void *Q, int NQ, const int32_t *q_rows, int M, const void *R
     if (rc) return rc;
     rc = maybe_repack(P.f, R, N, w + P.o_rr, stream, &r, 1);
     if (rc) return rc;
+    const int32_t *rows = nullptr;          // the caller's list with out-of-map entries replaced
+    if (q_rows) {
+        int32_t *safe = (int32_t *)(w + P.o_rows);
+        hipLaunchKernelGGL(nn_rows_kernel, dim3(std::min((M + 255) / 256, 4096)), dim3(256), 0, stream, q_rows, M, NQ,
+                           safe);
+        DDM_CHECK_LAUNCH();
+        rows = safe;
+    }
     SweepArgs a{};
-    a.Q = (const unsigned char *)q; a.R = (const unsigned char *)r; a.qrows = q_rows;
+    a.Q = (const unsigned char *)q; a.R = (const unsigned char *)r; a.qrows = rows;
     a.rowpart = (uint64_t *)(w + P.o_part);
     a.nq = M; a.nref = N; a.ld = P.f.ld; a.chunk = P.chunk; a.nchunks = P.nchunks; a.sb_per_wg = 1;
     a.rowcap = M;
     DDM_CHECK(launch_sweep(P.f, false, a, dim3(P.nchunks, P.qblocks, 1), stream));
     ResolveArgs ra{};
     ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = M;
-    ra.Q = a.Q; ra.qrows = q_rows; ra.nq = M; ra.R = a.R; ra.nref = N; ra.ld = P.f.ld; ra.d = P.f.d;
+    ra.Q = a.Q; ra.qrows = rows; ra.nq = M; ra.R = a.R; ra.nref = N; ra.ld = P.f.ld; ra.d = P.f.d;
     ra.neg_out = P.f.l2 ? 1 : 0;
     const int qb = resolve_qb(M);
-    DDM_DT_QB_SWITCH(P.f.dtype, qb, nn_resolve_kernel, dim3((M + qb - 1) / qb), dim3(256), 0, stream, ra, out_idx,
-                     out_score);
+    DDM_DT_QB_SWITCH(P.f.dtype, qb, nn_resolve_kernel, dim3((M + qb - 1) / qb), dim3(256), 0, stream, ra, q_rows,
+                     NQ, out_idx, out_score);
     DDM_CHECK_LAUNCH();
     return DDM_OK;
 }

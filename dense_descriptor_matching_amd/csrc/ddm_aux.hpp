@@ -174,9 +174,20 @@ struct ResolveArgs {
 
 __device__ __forceinline__ float reported(float s, int neg_out) { return neg_out ? fmaxf(-s, 0.f) : s; }
 
-// Plain NN output: out_idx[x], out_score[x] for every query.
+// Caller gather list -> the rows the sweep reads: entries outside [0, nrows)
+// become row 0 (so no access leaves the map) and are reported as -1 later.
+__global__ void __launch_bounds__(256) nn_rows_kernel(const int32_t *qrows, int n, int nrows, int32_t *safe) {
+    for (int x = blockIdx.x * 256 + threadIdx.x; x < n; x += gridDim.x * 256) {
+        const int r = qrows[x];
+        safe[x] = (r >= 0 && r < nrows) ? r : 0;
+    }
+}
+
+// Plain NN output: out_idx[x], out_score[x] for every query (-1 and NaN for a
+// caller row outside the query map; `given` holds the caller's list).
 template <int DT, int QB>
-__global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, int32_t *out_idx, float *out_score) {
+__global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, const int32_t *given, int nrows,
+                                                         int32_t *out_idx, float *out_score) {
     __shared__ uint64_t red[256];
     resolve_block<DT, QB, 256>(blockIdx.x, red, a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
                       [&](int x) {
@@ -184,7 +195,11 @@ __global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, int32_t 
                           return a.Q + (long long)qrow * a.ld * Tr<DT>::ESZ;
                       },
                       [&](bool valid, int x, int j, float s, int sub) {
-                          if (valid && sub == 0) { out_idx[x] = j; out_score[x] = reported(s, a.neg_out); }
+                          if (valid && sub == 0) {
+                              const bool ok = !given || (given[x] >= 0 && given[x] < nrows);
+                              out_idx[x] = ok ? j : -1;
+                              out_score[x] = ok ? reported(s, a.neg_out) : __builtin_nanf("");
+                          }
                       });
 }
 

@@ -82,7 +82,8 @@ int64_t ddm_seed_count(int H, int W, int grid_stride);
  * exact ties) of M query rows against all N reference rows.
  *   Q       [NQ][d] query map; query a is row q_rows[a] (or row a when q_rows
  *           is NULL, which needs NQ >= M)
- *   q_rows  device int32[M] with entries in [0, NQ), or NULL
+ *   q_rows  device int32[M] with entries in [0, NQ), or NULL; an entry outside
+ *           [0, NQ) reads no memory outside Q and yields out_idx -1, out_score NaN
  *   R       [N][d] reference map
  *   out_idx device int32[M]: NN index in [0, N)
  *   out_score device float[M]: the fp32 dot product of the pair

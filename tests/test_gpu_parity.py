@@ -64,6 +64,19 @@ def test_nn_gathered_rows(ddm):
     check_nn(dec(Q, synth.F16), dec(R, synth.F16), rows, idx.cpu().numpy(), s.cpu().numpy())
 
 
+def test_nn_gather_rows_outside_the_map(ddm):
+    """Entries of the gather list outside [0, NQ) read nothing outside Q and report -1 / NaN."""
+    import torch
+    Q = synth.gaussian_rows(300, 24, synth.F16, 12)
+    R = synth.gaussian_rows(2000, 24, synth.F16, 13)
+    rows = np.array([5, -1, 299, 300, 1 << 30, -(1 << 30), 0, 17], np.int32)
+    idx, s = ddm.nn(dev(Q, synth.F16), dev(R, synth.F16), q_rows=torch.from_numpy(rows).cuda())
+    idx, s = idx.cpu().numpy(), s.cpu().numpy()
+    bad = (rows < 0) | (rows >= 300)
+    assert (idx[bad] == -1).all() and np.isnan(s[bad]).all()
+    check_nn(dec(Q, synth.F16), dec(R, synth.F16), rows[~bad], idx[~bad], s[~bad])
+
+
 def test_nn_all_scores_negative(ddm):
     R = -np.abs(synth.gaussian_rows(1000, 8, synth.F32, 8)).astype(np.float32)
     Q = np.abs(synth.gaussian_rows(50, 8, synth.F32, 9)).astype(np.float32)
