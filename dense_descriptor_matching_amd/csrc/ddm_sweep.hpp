@@ -436,8 +436,12 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
     const int nslots = ngroups * GROUP;
 
     // ---- stage the chunk in LDS: slot c of tile t of group q <- reference q*GROUP + G*c + t.
-    // Each thread issues SU loads before storing any of them, so the staging
-    // waits for memory once per SU pieces rather than once per piece.
+    // Threads walk the LDS image in address order (piece slot qq at byte qq*PS:
+    // tile, then piece, then slot), so every store instruction writes one
+    // contiguous, bank-conflict-free run; the matching global reads gather 16
+    // rows G apart, which the cache serves since each group's rows are read
+    // whole. Each thread issues SU loads before storing any of them, so the
+    // staging waits for memory once per SU pieces rather than once per piece.
     {
         constexpr int SU = 8;
         const int total = nslots * np;
@@ -446,7 +450,9 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
 #pragma unroll
             for (int u = 0; u < SU; ++u) {
                 const int qq = base + u * NW * 64 + tid;
-                const int r = qq / np, pc = qq - r * np;
+                const int tile = qq / (np * 16), rem = qq - tile * (np * 16);
+                const int pc = rem >> 4, c = rem & 15;
+                const int r = (tile / G) * GROUP + G * c + tile % G;
                 v[u] = T::nan_piece();
                 if (qq < total && r < nvalid)
                     v[u] = *reinterpret_cast<const raw *>(R + ((long long)(r0 + r) * p.ld + pc * E) * ESZ);
@@ -455,11 +461,7 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
             for (int u = 0; u < SU; ++u) {
                 const int qq = base + u * NW * 64 + tid;
                 if (qq >= total) break;
-                const int r = qq / np, pc = qq - r * np;
-                const int grp = r / GROUP, w = r % GROUP;
-                const int tile = grp * G + (w % G);
-                const int c = w / G;
-                *reinterpret_cast<raw *>(lds + tile * TB + pc * 16 * PS + c * PS) = v[u];
+                *reinterpret_cast<raw *>(lds + (size_t)qq * PS) = v[u];
             }
         }
     }
