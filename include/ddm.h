@@ -21,7 +21,8 @@
  * Conventions shared by every entry point:
  *  - Maps are row-major [H][W][d] (pixel p = x + W*y, then d components),
  *    contiguous, in device memory, 16-byte aligned (fp16/bf16) or 4-byte
- *    aligned (fp32). Values must be finite. Element types: DDM_F32 (float),
+ *    aligned (fp32). Values must be finite, and dot products within the fp32
+ *    range (unit-norm descriptors are far inside). Element types: DDM_F32 (float),
  *    DDM_F16 (IEEE binary16), DDM_BF16 (bfloat16); products are accumulated in
  *    fp32 (fp16/bf16 products are exact in fp32).
  *  - All device buffers (inputs, outputs, workspace) belong to the caller. The
