@@ -4,7 +4,8 @@ R1 (NN): where the oracle's top-1/top-2 margin is >= tau the GPU index equals
 the oracle index; otherwise the GPU index must score within tau of the best.
 Scores always agree within tau with the exact score of the returned pair.
 R2 (mutual): every oracle pair whose two margins are >= tau is found; every GPU
-pair is an oracle pair or near-reciprocal (within tau of both maxima).
+pair is an oracle pair or near-reciprocal (within tau of both maxima); no
+image-2 pixel appears twice.
 R3 (FRM): seeds whose path never met a margin below tau have identical state
 (u, v, iteration of convergence); other seeds, when converged, end on a
 near-reciprocal pair; the GPU output is exactly its converged seed states,
@@ -44,6 +45,7 @@ def check_mutual(A, B, gi, gj, gs, ref=None, tau=TAU):
     m = ref if ref is not None else oracle.mutual(A, B)
     gi = np.asarray(gi); gj = np.asarray(gj)
     assert np.all(np.diff(gi) > 0), "GPU pairs not strictly ascending in i"
+    assert len(np.unique(gj)) == len(gj), "an image-2 pixel appears in two GPU pairs"
     gpu = set(zip(gi.tolist(), gj.tolist()))
     ref_set = set(zip(m["i"].tolist(), m["j"].tolist()))
     sharp = [(i, j) for i, j in ref_set if m["m12"][i] >= tau and m["m21"][j] >= tau]

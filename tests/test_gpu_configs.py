@@ -65,6 +65,7 @@ def test_mutual_512x384_sampled(ddm):
     N = 512 * 384
     # whole-output properties
     assert np.all(np.diff(gi) > 0) and len(gi) > 1000
+    assert len(np.unique(gj)) == len(gj), "an image-2 pixel is matched twice"
     assert np.array_equal(nn12[gi], gj) and np.array_equal(s12[gi], gs)
     rng = np.random.default_rng(123)
     rows = np.unique(np.concatenate([rng.choice(N, 320, replace=False), gi[rng.choice(len(gi), 64, replace=False)]]))
