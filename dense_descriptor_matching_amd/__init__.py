@@ -95,6 +95,16 @@ def _stream():
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _on(*tensors):
+    """Make the tensors' device current for the call (the library launches on the current
+    device and the caller's current stream there); all tensors must share that device."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError(f"tensors on {dev} and {t.device}: one device per call")
+    return torch.cuda.device(dev)
+
+
 def _check_map(D, name):
     if not isinstance(D, torch.Tensor) or not D.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
@@ -178,8 +188,9 @@ def nn(Q: torch.Tensor, R: torch.Tensor, q_rows: torch.Tensor | None = None, met
     if nbytes == 0:
         raise DDMError(-4, "ddm_nn_ex_workspace_bytes (unsupported dtype, d or metric)")
     ws = _workspace(nbytes, Q.device)
-    _rc(L.ddm_nn_ex(_ptr(Q), NQ, _ptr(q_rows), M, _ptr(R), N, d, _DT[Q.dtype], mt, _ptr(out_idx), _ptr(out_s),
-                    _ptr(ws), ws.numel(), _stream()), "ddm_nn_ex")
+    with _on(Q, R, q_rows, out_idx, ws):
+        _rc(L.ddm_nn_ex(_ptr(Q), NQ, _ptr(q_rows), M, _ptr(R), N, d, _DT[Q.dtype], mt, _ptr(out_idx), _ptr(out_s),
+                        _ptr(ws), ws.numel(), _stream()), "ddm_nn_ex")
     return out_idx, out_s
 
 
@@ -223,17 +234,19 @@ def frm_match_into(D1, D2, grid_stride, max_iter, buf: FrmBuffers, batched: bool
         B2, H2, W2, _ = D2.shape
         if B2 != B:
             raise ValueError("batch sizes differ")
-        _rc(L.ddm_frm_match_batched(B, _ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride, max_iter,
-                                    _ptr(buf.out_i), _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count),
-                                    _ptr(buf.state), _ptr(buf.qcounts), _ptr(buf.ws), buf.ws.numel(), _stream()),
-            "ddm_frm_match_batched")
+        with _on(D1, D2, buf.out_i, buf.ws):
+            _rc(L.ddm_frm_match_batched(B, _ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride, max_iter,
+                                        _ptr(buf.out_i), _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count),
+                                        _ptr(buf.state), _ptr(buf.qcounts), _ptr(buf.ws), buf.ws.numel(), _stream()),
+                "ddm_frm_match_batched")
     else:
         H1, W1, d = D1.shape
         H2, W2, _ = D2.shape
-        _rc(L.ddm_frm_match(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride, max_iter,
-                            _ptr(buf.out_i), _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count),
-                            _ptr(buf.state), _ptr(buf.qcounts), _ptr(buf.ws), buf.ws.numel(), _stream()),
-            "ddm_frm_match")
+        with _on(D1, D2, buf.out_i, buf.ws):
+            _rc(L.ddm_frm_match(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, grid_stride, max_iter,
+                                _ptr(buf.out_i), _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count),
+                                _ptr(buf.state), _ptr(buf.qcounts), _ptr(buf.ws), buf.ws.numel(), _stream()),
+                "ddm_frm_match")
 
 
 def frm_match(D1: torch.Tensor, D2: torch.Tensor, grid_stride: int = 8, max_iter: int = 10,
@@ -327,10 +340,11 @@ def frm_match_ex(D1: torch.Tensor, D2: torch.Tensor, *, grid_stride: int = 8, st
     if nbytes == 0:
         raise DDMError(-1, "ddm_frm_ex_workspace_bytes")
     ws = _workspace(nbytes, dev)
-    _rc(L.ddm_frm_match_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, mt, grid_stride,
-                           _ptr(starts) if n >= 0 else None, max(n, 0), max_iter, float(pixel_tol), _ptr(basin),
-                           _ptr(out_i), _ptr(out_j), _ptr(out_s), cap, _ptr(count), _ptr(state), _ptr(qc),
-                           _ptr(ws), ws.numel(), _stream()), "ddm_frm_match_ex")
+    with _on(D1, D2, out_i, ws):
+        _rc(L.ddm_frm_match_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, dt, mt, grid_stride,
+                               _ptr(starts) if n >= 0 else None, max(n, 0), max_iter, float(pixel_tol), _ptr(basin),
+                               _ptr(out_i), _ptr(out_j), _ptr(out_s), cap, _ptr(count), _ptr(state), _ptr(qc),
+                               _ptr(ws), ws.numel(), _stream()), "ddm_frm_match_ex")
     m = _count(count[0].item())
     res = (out_i[:m].clone(), out_j[:m].clone(), out_s[:m].clone())
     if ret_basin:
@@ -370,9 +384,10 @@ def c2f_match(F1: torch.Tensor, F2: torch.Tensor, *, factor: int = 2, coarse_str
     count = torch.zeros(1, dtype=torch.int32, device=dev)
     crops = torch.empty(tiles * 5, dtype=torch.int32, device=dev)
     ws = _workspace(nbytes, dev)
-    _rc(L.ddm_c2f_match(_ptr(F1), H1, W1, _ptr(F2), H2, W2, d, dt, factor, coarse_stride, coarse_iter, ch, cw,
-                        fine_stride, fine_iter, _ptr(out_i), _ptr(out_j), _ptr(out_s), cap, _ptr(count),
-                        _ptr(crops), _ptr(ws), ws.numel(), _stream()), "ddm_c2f_match")
+    with _on(F1, F2, out_i, ws):
+        _rc(L.ddm_c2f_match(_ptr(F1), H1, W1, _ptr(F2), H2, W2, d, dt, factor, coarse_stride, coarse_iter, ch, cw,
+                            fine_stride, fine_iter, _ptr(out_i), _ptr(out_j), _ptr(out_s), cap, _ptr(count),
+                            _ptr(crops), _ptr(ws), ws.numel(), _stream()), "ddm_c2f_match")
     n = _count(count[0].item())
     res = (out_i[:n].clone(), out_j[:n].clone(), out_s[:n].clone())
     return res + (crops.view(tiles, 5),) if return_crops else res
@@ -402,9 +417,11 @@ def mutual_nn_into(D1, D2, buf: MutualBuffers):
         raise ValueError("D1 and D2 must share dtype and d")
     H1, W1, d = D1.shape
     H2, W2, _ = D2.shape
-    _rc(lib().ddm_mutual_nn_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, _DT[D1.dtype], buf.metric, _ptr(buf.out_i),
-                               _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count), _ptr(buf.nn12),
-                               _ptr(buf.s12), _ptr(buf.ws), buf.ws.numel(), _stream()), "ddm_mutual_nn_ex")
+    with _on(D1, D2, buf.out_i, buf.ws):
+        _rc(lib().ddm_mutual_nn_ex(_ptr(D1), H1, W1, _ptr(D2), H2, W2, d, _DT[D1.dtype], buf.metric,
+                                   _ptr(buf.out_i), _ptr(buf.out_j), _ptr(buf.out_s), buf.cap, _ptr(buf.count),
+                                   _ptr(buf.nn12), _ptr(buf.s12), _ptr(buf.ws), buf.ws.numel(), _stream()),
+            "ddm_mutual_nn_ex")
 
 
 def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False, metric: str = "dot"):
@@ -422,6 +439,7 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False, metri
     return res
 
 
-__all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "c2f_match", "mutual_nn", "mutual_nn_into", "seed_count",
-           "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH", "profile_enable", "profile_read",
-           "frm_set_mode", "frm_get_mode", "FRM_PER_HALF_STEP", "FRM_LOOP"]
+__all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "c2f_match", "mutual_nn",
+           "mutual_nn_into", "seed_count", "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH",
+           "profile_enable", "profile_read", "frm_set_mode", "frm_get_mode", "frm_set_barrier_polls",
+           "FRM_PER_HALF_STEP", "FRM_LOOP", "METRICS"]
