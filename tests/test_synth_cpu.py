@@ -18,3 +18,61 @@ def test_large_shift_pair_is_an_exact_shift():
     assert np.abs(n - 1).max() < 2e-3
     again = synth.large_shift_pair(H, W, 8, synth.F16, 3, (dx, dy))
     assert np.array_equal(again.D1, p.D1) and np.array_equal(again.D2, p.D2)
+
+
+def test_same_seed_same_bits_and_shapes():
+    a = synth.make_pair(40, 30, 24, synth.F16, 5, sigma=0.1, shift=(3, -2))
+    b = synth.make_pair(40, 30, 24, synth.F16, 5, sigma=0.1, shift=(3, -2))
+    c = synth.make_pair(40, 30, 24, synth.F16, 6, sigma=0.1, shift=(3, -2))
+    assert a.D1.shape == a.D2.shape == (40, 30, 24) and a.D1.dtype == np.float16
+    assert np.array_equal(a.D1, b.D1) and np.array_equal(a.D2, b.D2)
+    assert not np.array_equal(a.D1, c.D1)
+    bf = synth.make_pair(8, 6, 16, synth.BF16, 5, sigma=0.1)
+    assert bf.D1.dtype == np.uint16 and bf.D1.shape == (8, 6, 16)
+
+
+def test_bf16_rounding_is_nearest_even():
+    # halfway cases between two bf16 values (low 16 bits 0x8000) round to the even one
+    x = np.array([0x3F808000, 0x3F818000, 0x3F80_7FFF, 0x3F80_8001, 0xBF818000], np.uint32).view(np.float32)
+    got = synth.f32_to_bf16_bits(x)
+    assert got.tolist() == [0x3F80, 0x3F82, 0x3F80, 0x3F81, 0xBF82]
+    # and every value lands on the nearer neighbour
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(20000).astype(np.float32)
+    r = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(v)).astype(np.float64)
+    u = v.view(np.uint32)
+    lo = (u & 0xFFFF0000).view(np.float32).astype(np.float64)
+    hi = ((u & 0xFFFF0000) + 0x10000).astype(np.uint32).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(r - v) <= np.minimum(np.abs(v - lo), np.abs(v - hi)) + 0)
+
+
+def test_fp16_rounding_matches_numpy_nearest_even():
+    x = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, -(1 + 2 ** -11)], np.float64)   # exact halfway cases
+    got = synth.cast_stored(x, synth.F16)
+    assert got.tolist() == [1.0, 1 + 2 ** -9, -1.0]
+
+
+def test_shift_in_range_fraction_and_rows():
+    H, W, dx, dy = 512, 384, 17, -9
+    p = synth.make_pair(H, W, 8, synth.F32, 3, sigma=0.1, shift=(dx, dy))
+    frac_out = p.meta["out_of_range"] / (H * W)
+    expect = 1 - (W - abs(dx)) * (H - abs(dy)) / (H * W)
+    assert abs(frac_out - expect) < 1e-12 and 0.05 < frac_out < 0.07      # ≈ 6.1 % at the headline shift
+    n = np.linalg.norm(p.D2.astype(np.float64), axis=-1)
+    assert np.abs(n - 1).max() < 1e-6
+
+
+def test_occlusion_area_near_thirty_percent():
+    (p,) = synth.make_config("hard_frm_512x512x64_bf16")
+    x0, y0, w, h = p.meta["occlusion"]
+    assert w == h == 280 and abs(w * h / (512 * 512) - 0.3) < 0.01
+    assert 0 <= x0 <= 512 - w and 0 <= y0 <= 512 - h
+    assert p.meta["rotate_deg"] == 20.0
+
+
+def test_batched_config_shifts_in_range():
+    pairs = synth.make_config("batched_frm_16x512x384x24_f16")
+    assert len(pairs) == 16
+    shifts = [pr.meta["shift"] for pr in pairs]
+    assert all(-32 <= dx <= 32 and -32 <= dy <= 32 for dx, dy in shifts)
+    assert len(set(shifts)) > 8
