@@ -105,6 +105,12 @@ template <> struct Tr<DT_F32> {
     }
 };
 
+// 16-byte NaN pieces in device memory, the source of chunk slots past the end
+// of a map when the chunk is staged with direct-to-LDS loads.
+__device__ const uint32_t kNanPiece16[2][4] = {{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u},
+                                               {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}};
+__device__ __forceinline__ const uint32_t *nan_piece16(int dt) { return kNanPiece16[dt == DT_BF16 ? 1 : 0]; }
+
 struct SweepArgs {
     const unsigned char *Q;      // query map of pair 0
     const unsigned char *R;      // reference map of pair 0
@@ -436,13 +442,30 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
     const int nslots = ngroups * GROUP;
 
     // ---- stage the chunk in LDS: slot c of tile t of group q <- reference q*GROUP + G*c + t.
-    // Threads walk the LDS image in address order (piece slot qq at byte qq*PS:
-    // tile, then piece, then slot), so every store instruction writes one
-    // contiguous, bank-conflict-free run; the matching global reads gather 16
-    // rows G apart, which the cache serves since each group's rows are read
-    // whole. Each thread issues SU loads before storing any of them, so the
-    // staging waits for memory once per SU pieces rather than once per piece.
-    {
+    // The LDS image is written in address order (piece slot qq at byte qq*PS:
+    // tile, then piece, then slot); the matching global reads gather 16 rows G
+    // apart, which the cache serves since each group's rows are read whole.
+    if constexpr (PS == 16) {
+        // 16-byte pieces: global_load_lds_dwordx4 moves each lane's piece straight
+        // into LDS at the wave's base + 16 * lane, so a wave fills 1 KB per
+        // instruction with no register round trip, and every load of the chunk is
+        // in flight before the single wait. Slots past the map read a NaN piece.
+        const int total = nslots * np;
+        for (int base = wave * 64; base < total; base += NW * 64) {
+            const int qq = base + lane;
+            const int tile = qq / (np * 16), rem = qq - tile * (np * 16);
+            const int pc = rem >> 4, c = rem & 15;
+            const int r = (tile / G) * GROUP + G * c + tile % G;
+            const unsigned char *src = (r < nvalid) ? R + ((long long)(r0 + r) * p.ld + pc * E) * ESZ
+                                                    : reinterpret_cast<const unsigned char *>(nan_piece16(DT));
+            if (qq < total)
+                __builtin_amdgcn_global_load_lds(
+                    (const void __attribute__((address_space(1))) *)src,
+                    (void __attribute__((address_space(3))) *)(lds + (size_t)base * 16), 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);        // every counter at zero: this wave's LDS loads have landed
+    } else {
+        // 4-byte pieces (fp32 maps): SU loads per thread in flight before their stores.
         constexpr int SU = 8;
         const int total = nslots * np;
         for (int base = 0; base < total; base += SU * NW * 64) {
