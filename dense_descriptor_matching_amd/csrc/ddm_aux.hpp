@@ -26,6 +26,7 @@ namespace ddm {
 template <int DT>
 __device__ __forceinline__ float dot_rows(const unsigned char *a, const unsigned char *b, int d) {
     float s = 0.f;
+#pragma unroll 8      // loads of eight elements in flight together; the fma chain keeps element order
     for (int k = 0; k < d; ++k) s = fmaf(Tr<DT>::elem(a, k), Tr<DT>::elem(b, k), s);
     return s;
 }
@@ -86,6 +87,7 @@ __device__ __forceinline__ void rescan_one(uint64_t k, const unsigned char *qp, 
             acc[c] = 0.f;
         }
         const int np = ld / 8;
+#pragma unroll 4      // four pieces' loads in flight together instead of one latency per piece
         for (int p = 0; p < np; ++p) {
             const u32x4_t qv = q4[p];
 #pragma unroll
