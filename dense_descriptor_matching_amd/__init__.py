@@ -71,6 +71,7 @@ def _declare(lib):
     lib.ddm_frm_set_mode.argtypes = [I]; lib.ddm_frm_set_mode.restype = I
     lib.ddm_frm_get_mode.argtypes = []; lib.ddm_frm_get_mode.restype = I
     lib.ddm_frm_set_barrier_polls.argtypes = [I]; lib.ddm_frm_set_barrier_polls.restype = I
+    lib.ddm_debug_set_grid_cap.argtypes = [I]; lib.ddm_debug_set_grid_cap.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
     lib.ddm_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]; lib.ddm_profile_read.restype = I
     return lib
@@ -149,6 +150,12 @@ def frm_set_barrier_polls(polls: int):
     """Polls a grid-barrier wait of the loop mode makes before it gives up (0: the default).
     A test aid: a tiny value makes loop-mode calls report failure instead of matches."""
     _rc(lib().ddm_frm_set_barrier_polls(polls), "ddm_frm_set_barrier_polls")
+
+
+def debug_set_grid_cap(max_workgroups: int):
+    """Cap the grid of the FRM phase kernels (0: no cap); outputs must not change with it.
+    A test aid against dependences between concurrent workgroups."""
+    _rc(lib().ddm_debug_set_grid_cap(max_workgroups), "ddm_debug_set_grid_cap")
 
 
 def profile_enable(mask: int):
@@ -442,4 +449,5 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False, metri
 __all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "c2f_match", "mutual_nn",
            "mutual_nn_into", "seed_count", "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH",
            "profile_enable", "profile_read", "frm_set_mode", "frm_get_mode", "frm_set_barrier_polls",
+           "debug_set_grid_cap",
            "FRM_PER_HALF_STEP", "FRM_LOOP", "METRICS"]

@@ -166,6 +166,15 @@ hipError_t fmt_dispatch(const MapFmt &f, Fn &&fn) {
     }
 }
 
+// Test aid: upper bound on the grid of the FRM phase kernels, which stride their
+// tasks over whatever grid they get (0 = none). Results must not depend on it;
+// a bound of 1 runs every task in one workgroup.
+std::atomic<int> &frm_grid_cap() { static std::atomic<int> n{0}; return n; }
+long long capped_grid(long long g) {
+    const int cap = frm_grid_cap().load();
+    return cap > 0 ? std::min<long long>(g, cap) : g;
+}
+
 // FRM phase kernels of one map format. which = 0: per-half-step sweep of
 // half-step h (plain launch), 1: loop kernel from half-step h (cooperative
 // launch). The grid is min(ntask, workgroups the device keeps resident).
@@ -191,7 +200,8 @@ hipError_t launch_frm_t(int which, const FrmArgs *a, int h, size_t lds, long lon
                                                          nw * 64, lds);
     if (e != hipSuccess) return e;
     if (per_cu < 1 || ncu < 1) return hipErrorInvalidConfiguration;
-    const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(ntask, (long long)per_cu * ncu));
+    const unsigned grid =
+        (unsigned)std::max<long long>(1, capped_grid(std::min<long long>(ntask, (long long)per_cu * ncu)));
     if (which == 0) {
         hipLaunchKernelGGL(ks, dim3(grid), dim3(nw * 64), lds, s, *a, h);
         return hipGetLastError();
@@ -571,7 +581,7 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
         const long long upd_tasks = (long long)P.B * ((P.k + 15) / 16);
         for (int h = 0; h < std::min(h_loop, P.nhalf); ++h) {
             DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, 0, &fa, h, P.loop_lds, sweep_tasks, s, true); }));
-            DDM_DT_SWITCH(f.dtype, frm_update_kernel, dim3((unsigned)std::min<long long>(upd_tasks, 2048)),
+            DDM_DT_SWITCH(f.dtype, frm_update_kernel, dim3((unsigned)capped_grid(std::min<long long>(upd_tasks, 2048))),
                           dim3(256), 0, s, fa, h);
             DDM_CHECK_LAUNCH();
         }
@@ -835,6 +845,12 @@ int ddm_frm_set_mode(int mode) {
 
 int ddm_frm_get_mode(void) { return frm_mode().load(); }
 
+int ddm_debug_set_grid_cap(int max_workgroups) {
+    if (max_workgroups < 0) return DDM_ERR_INVALID;
+    frm_grid_cap().store(max_workgroups);
+    return DDM_OK;
+}
+
 int ddm_frm_set_barrier_polls(int polls) {
     if (polls < 0) return DDM_ERR_INVALID;
     loop_spin_limit().store(polls == 0 ? kSpinLimit : polls);
@@ -962,7 +978,7 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
                           (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, (uint64_t)h_loop,
                           (uint64_t)(uintptr_t)O.starts, (uint64_t)(uint32_t)O.n_starts, tol_bits,
                           (uint64_t)(uintptr_t)O.basin, (uint64_t)metric,
-                          (uint64_t)(h_loop == 0 ? loop_spin_limit().load() : 0)};
+                          (uint64_t)(h_loop == 0 ? loop_spin_limit().load() : 0), (uint64_t)frm_grid_cap().load()};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return frm_run(P, O, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts,
                        workspace, s, h_loop);
@@ -1041,7 +1057,7 @@ int ddm_c2f_match(const void *F1, int H1, int W1, const void *F2, int H2, int W2
                           (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)crop_info,
                           (uint64_t)(uintptr_t)workspace, (uint64_t)loop,
-                          (uint64_t)(loop ? loop_spin_limit().load() : 0)};
+                          (uint64_t)(loop ? loop_spin_limit().load() : 0), (uint64_t)frm_grid_cap().load()};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return c2f_run(P, F1, F2, out_i, out_j, out_score, capacity, out_count, crop_info, workspace, s, loop);
     });

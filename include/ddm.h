@@ -189,6 +189,11 @@ int ddm_frm_get_mode(void);
  * time out on purpose; the kernel still ends and out_count reads -1. Process-wide; graph-cached
  * calls keep the value they were recorded with. */
 int ddm_frm_set_barrier_polls(int polls);
+/* Test aid against races between workgroups: caps the grid of the FRM sweep, update and loop
+ * kernels (which stride their tasks over whatever grid they get) at max_workgroups; 0 removes
+ * the cap. Outputs must be bit-identical with any cap; 1 runs every task in one workgroup.
+ * Process-wide; graph-cached calls keep the value they were recorded with. */
+int ddm_debug_set_grid_cap(int max_workgroups);
 
 /* ----------------------------------------------------- coarse-to-fine ---
  * Matching of maps larger than the network's 512-px input ("MASt3R" note on cv-learn.com,

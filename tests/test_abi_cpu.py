@@ -41,6 +41,12 @@ def test_frm_mode_switch(L):
     assert L.ddm_frm_set_mode(0) == 0 and L.ddm_frm_get_mode() == 0
 
 
+def test_grid_cap_setter(L):
+    assert L.ddm_debug_set_grid_cap(-1) == -1
+    assert L.ddm_debug_set_grid_cap(4) == 0
+    assert L.ddm_debug_set_grid_cap(0) == 0
+
+
 def test_barrier_polls_setter(L):
     assert L.ddm_frm_set_barrier_polls(-1) == -1
     assert L.ddm_frm_set_barrier_polls(3) == 0

@@ -245,3 +245,44 @@ def test_frm_modes_agree(ddm, name, S, it, batched):
     for what, r in runs[1:]:
         _assert_same(r, ref, f"{name} {what}")
     print(f"{name} S={S} it={it}: counts={ref[0].tolist()[:4]} queries={ref[3].reshape(len(pairs), -1)[0][:8].tolist()}")
+
+
+GRID_CAP_CASES = [
+    # (pairs, stride, max_iter, batched, caps)
+    (lambda: synth.make_config("tiny_frm_64x48x24_f32"), 8, 10, False, (1, 2)),
+    (lambda: [synth.make_pair(128, 96, 24, synth.F16, 71, sigma=0.2, shift=(5, -3))], 4, 10, False, (1, 3, 7)),
+    (lambda: [synth.make_pair(96, 80, 64, synth.BF16, 72 + b, sigma=0.3, shift=(b, -b)) for b in range(4)],
+     4, 10, True, (1, 5)),
+    (lambda: synth.make_config("frm_512x384x24_f16"), 8, 10, False, (1,)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GRID_CAP_CASES)))
+def test_frm_grid_cap_does_not_change_results(ddm, case):
+    """The FRM phase kernels stride their tasks over the grid they get; with the grid capped at
+    1, a few or many workgroups, in both execution modes, every output is bit-identical (no
+    dependence on how tasks spread over concurrent workgroups)."""
+    import torch
+    make, S, it, batched, caps = GRID_CAP_CASES[case]
+    pairs = make()
+    D1 = torch.stack([dev(p.D1, p.dtype) for p in pairs]); D2 = torch.stack([dev(p.D2, p.dtype) for p in pairs])
+    if not batched:
+        D1, D2 = D1[0], D2[0]
+    p0 = pairs[0]
+    buf = ddm.FrmBuffers(len(pairs), p0.H1, p0.W1, p0.H2, p0.W2, p0.d, D1.dtype, S, it, D1.device)
+    ref = None
+    try:
+        for mode in (ddm.FRM_PER_HALF_STEP, ddm.FRM_LOOP):
+            ddm.frm_set_mode(mode)
+            for cap in (0,) + tuple(caps):
+                ddm.debug_set_grid_cap(cap)
+                buf.count.fill_(-3); buf.qcounts.fill_(-3); buf.state.fill_(-3)
+                ddm.frm_match_into(D1, D2, S, it, buf, batched=batched)
+                got = _frm_outputs(buf)
+                if ref is None:
+                    ref = got
+                else:
+                    _assert_same(got, ref, f"mode {mode} cap {cap}")
+    finally:
+        ddm.debug_set_grid_cap(0)
+        ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
