@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
 ]
 
 
+DEMO_SRC = os.path.join(ROOT, "tests", "c_abi_demo.cpp")
+DEMO = os.path.join(ROOT, "tests", "c_abi_demo")
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
@@ -32,7 +36,19 @@ def build(verbose: bool = False) -> str:
     if verbose and r.stderr:
         print(r.stderr)
     os.replace(tmp, LIB)
+    build_demo(hipcc)
     return LIB
+
+
+def build_demo(hipcc: str) -> str:
+    """The plain host program that drives the C ABI in tests (links libddm.so by rpath)."""
+    cmd = [hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), "-o", DEMO + ".tmp", DEMO_SRC,
+           "-L", HERE, "-lddm", "-Wl,-rpath,$ORIGIN/../dense_descriptor_matching_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the ABI demo ({r.returncode}):\n{r.stderr}")
+    os.replace(DEMO + ".tmp", DEMO)
+    return DEMO
 
 
 if __name__ == "__main__":

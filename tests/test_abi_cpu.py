@@ -225,3 +225,14 @@ def test_binding_refuses_cpu_tensors():
         ddm.frm_match(x, x)
     with pytest.raises(TypeError):
         ddm.mutual_nn(x, x)
+
+
+def test_c_abi_demo_is_built_and_links():
+    """The plain host program of the GPU ABI test exists and resolves libddm.so (no args:
+    it prints its usage before touching the GPU)."""
+    import os
+    import subprocess
+    demo = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_demo")
+    assert os.path.exists(demo), "build with __graft_entry__.build()"
+    r = subprocess.run([demo], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "usage" in r.stderr
