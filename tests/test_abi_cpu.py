@@ -78,6 +78,10 @@ def test_workspace_sizes(L):
     assert L.ddm_frm_workspace_bytes(1, 512, 384, 512, 384, 24, 1, 8, 0) == 0
     assert L.ddm_mutual_workspace_bytes(0, 384, 512, 384, 24, 1) == 0
     assert L.ddm_nn_workspace_bytes(1, 1, 1, 129, 1) == 0
+    # the per-map pixel limit (2^27, H*W*16 < 2^31): at the limit sizes are reported, above it 0
+    assert L.ddm_frm_workspace_bytes(1, 1 << 13, 1 << 14, 64, 48, 24, 1, 1024, 1) > 0
+    assert L.ddm_frm_workspace_bytes(1, 1 << 14, 1 << 14, 64, 48, 24, 1, 1024, 1) == 0
+    assert L.ddm_mutual_workspace_bytes(1 << 14, 1 << 14, 4, 4, 24, 1) == 0
 
 
 FAKE = 1 << 40        # 16-byte aligned, never dereferenced: every case fails validation first
@@ -107,6 +111,8 @@ def test_frm_rejects_bad_arguments(L):
     assert _frm(L, cap=47) == -2
     assert _frm(L, ws=None) == -3
     assert _frm(L, wsb=16) == -3
+    assert _frm(L, H1=1 << 14, W1=1 << 14) == -1          # 2^28 pixels: above the per-map limit
+    assert _frm(L, H2=1 << 13, W2=(1 << 14) + 1) == -1    # just above 2^27
     assert _frm(L, D1=FAKE + 2) == -1          # fp16 map not 16-byte aligned
     assert _frm(L, D2=FAKE + 2, dtype=0) == -1          # fp32 map not 4-byte aligned
 
