@@ -209,6 +209,32 @@ def large_shift_pair(H: int, W: int, d: int, dtype: int, seed: int, shift) -> Pa
     return Pair(D1, D2, dtype, name=f"large_shift_{H}x{W}x{d}", meta={"shift": (dx, dy)})
 
 
+def large_shift_pair_device(H: int, W: int, d: int, dtype: int, seed: int, shift, device, band: int = 256):
+    """As large_shift_pair, drawn on the device (torch's seeded Philox generator, fp32, in
+    bands of rows) for maps too large to build on the host: returns (D1, D2) device tensors
+    of the stored type (torch.float16 / torch.bfloat16)."""
+    import torch
+    tdt = {F16: torch.float16, BF16: torch.bfloat16}[dtype]
+    dx, dy = shift
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw():
+        out = torch.empty((H, W, d), dtype=tdt, device=device)
+        for y0 in range(0, H, band):
+            x = torch.randn((min(band, H - y0), W, d), generator=g, device=device, dtype=torch.float32)
+            x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+            out[y0:y0 + x.shape[0]] = x.to(tdt)
+            del x
+        return out
+
+    D1 = draw()
+    D2 = draw()
+    D2[max(0, -dy):min(H, H - dy), max(0, -dx):min(W, W - dx)] = \
+        D1[max(0, dy):min(H, H + dy), max(0, dx):min(W, W + dx)]
+    return D1, D2
+
+
 def gaussian_rows(n: int, d: int, dtype: int, seed: int, unit: bool = True) -> np.ndarray:
     """n descriptor rows [n, d] in stored form (NN unit cases with arbitrary n)."""
     rng = np.random.Generator(np.random.PCG64(seed))

@@ -50,3 +50,27 @@ def test_frm_4096x4096_pure_shift(ddm):
     assert qc[0] == len(seeds) and qc[1] == len(seeds) and (qc[2:] == 0).all()
     del D1, D2
     torch.cuda.empty_cache()
+
+
+def test_frm_at_the_pixel_limit_pure_shift(ddm):
+    """Maps of 8192 x 16384 = 2^27 pixels, the per-map limit (6.4 GB each in fp16; 43,691
+    reference chunks), drawn on the device: every seed of a stride-512 grid ends on its
+    shifted counterpart in iteration 1."""
+    import torch
+    H, W = 8192, 16384
+    dx, dy = 5, -3
+    D1, D2 = synth.large_shift_pair_device(H, W, 24, synth.F16, 91, (dx, dy), "cuda")
+    print(f"{H}x{W}x24 f16 pure shift {dx},{dy}: maps drawn on the device", flush=True)
+    S = 512
+    i, j, s, st = ddm.frm_match(D1, D2, S, 4, return_state=True)
+    state = st["state"].cpu().numpy()
+    seeds = oracle.seed_grid(H, W, S)
+    assert len(seeds) == 16 * 32 and state.shape[0] == len(seeds)
+    assert seeds.max() > (1 << 26)
+    assert np.array_equal(state[:, 0], seeds)
+    assert np.array_equal(state[:, 1], seeds - dx - dy * W)
+    assert (state[:, 2] == 1).all()
+    assert np.array_equal(i.cpu().numpy(), seeds) and np.array_equal(j.cpu().numpy(), seeds - dx - dy * W)
+    assert np.abs(s.cpu().numpy() - 1.0).max() < 5e-3
+    del D1, D2
+    torch.cuda.empty_cache()

@@ -76,3 +76,19 @@ def test_batched_config_shifts_in_range():
     shifts = [pr.meta["shift"] for pr in pairs]
     assert all(-32 <= dx <= 32 and -32 <= dy <= 32 for dx, dy in shifts)
     assert len(set(shifts)) > 8
+
+
+def test_device_drawn_shift_pair_is_an_exact_shift():
+    """The device-side generator of the pixel-limit test, run on the CPU device at a tiny size."""
+    import torch
+    H, W, dx, dy = 24, 40, 5, -3
+    D1, D2 = synth.large_shift_pair_device(H, W, 8, synth.F16, 9, (dx, dy), "cpu", band=7)
+    assert D1.dtype == torch.float16 and D1.shape == (H, W, 8)
+    a, b = D1.numpy(), D2.numpy()
+    for y in range(H):
+        for x in range(W):
+            if 0 <= x + dx < W and 0 <= y + dy < H:
+                assert np.array_equal(b[y, x], a[y + dy, x + dx])
+    assert np.abs(np.linalg.norm(a.astype(np.float64), axis=-1) - 1).max() < 2e-3
+    E1, _ = synth.large_shift_pair_device(H, W, 8, synth.F16, 9, (dx, dy), "cpu", band=7)
+    assert torch.equal(E1, D1)
