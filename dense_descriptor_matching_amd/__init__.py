@@ -70,6 +70,7 @@ def _declare(lib):
     lib.ddm_c2f_match.restype = I
     lib.ddm_frm_set_mode.argtypes = [I]; lib.ddm_frm_set_mode.restype = I
     lib.ddm_frm_get_mode.argtypes = []; lib.ddm_frm_get_mode.restype = I
+    lib.ddm_frm_set_tail_after.argtypes = [I]; lib.ddm_frm_set_tail_after.restype = I
     lib.ddm_frm_set_barrier_polls.argtypes = [I]; lib.ddm_frm_set_barrier_polls.restype = I
     lib.ddm_debug_set_grid_cap.argtypes = [I]; lib.ddm_debug_set_grid_cap.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
@@ -133,8 +134,10 @@ def to_xy(idx: torch.Tensor, W: int):
     return idx % W, torch.div(idx, W, rounding_mode="floor")
 
 
-FRM_PER_HALF_STEP = 0      # one sweep + one update launch per half-step (default)
+FRM_PER_HALF_STEP = 0      # one sweep + one update launch per half-step
 FRM_LOOP = 1               # every iteration in one cooperative loop kernel
+FRM_TAIL = 2               # first iterations per half-step, the rest in one ticket-ordered tail kernel
+FRM_DEFAULT = FRM_TAIL
 
 
 def frm_set_mode(mode: int):
@@ -146,8 +149,14 @@ def frm_get_mode() -> int:
     return lib().ddm_frm_get_mode()
 
 
+def frm_set_tail_after(iterations: int):
+    """Iterations run per half-step before the tail kernel takes over in FRM_TAIL mode
+    (-1, the default: one for small problems, three for large ones)."""
+    _rc(lib().ddm_frm_set_tail_after(iterations), "ddm_frm_set_tail_after")
+
+
 def frm_set_barrier_polls(polls: int):
-    """Polls a grid-barrier wait of the loop mode makes before it gives up (0: the default).
+    """Polls a wait of the loop or tail kernel makes before it gives up (0: the default).
     A test aid: a tiny value makes loop-mode calls report failure instead of matches."""
     _rc(lib().ddm_frm_set_barrier_polls(polls), "ddm_frm_set_barrier_polls")
 
@@ -449,5 +458,5 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False, metri
 __all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "c2f_match", "mutual_nn",
            "mutual_nn_into", "seed_count", "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH",
            "profile_enable", "profile_read", "frm_set_mode", "frm_get_mode", "frm_set_barrier_polls",
-           "debug_set_grid_cap",
-           "FRM_PER_HALF_STEP", "FRM_LOOP", "METRICS"]
+           "debug_set_grid_cap", "frm_set_tail_after",
+           "FRM_PER_HALF_STEP", "FRM_LOOP", "FRM_TAIL", "FRM_DEFAULT", "METRICS"]

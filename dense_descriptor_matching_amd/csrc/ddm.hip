@@ -177,7 +177,8 @@ long long capped_grid(long long g) {
 
 // FRM phase kernels of one map format. which = 0: per-half-step sweep of
 // half-step h (plain launch), 1: loop kernel from half-step h (cooperative
-// launch). The grid is min(ntask, workgroups the device keeps resident).
+// launch), 2: tail kernel from half-step h (plain launch). The grid is
+// min(ntask, workgroups the device keeps resident).
 // launch == false only raises the kernels' dynamic-LDS limit.
 template <int DT, int NP, int NKB>
 hipError_t launch_frm_t(int which, const FrmArgs *a, int h, size_t lds, long long ntask, hipStream_t s,
@@ -186,24 +187,29 @@ hipError_t launch_frm_t(int which, const FrmArgs *a, int h, size_t lds, long lon
     constexpr int nw = nw_for(DT);
     auto ks = frm_sweep_kernel<DT, NP, NKB, rq, nw>;
     auto kl = frm_loop_kernel<DT, NP, NKB, rq, nw>;
+    auto kt = frm_tail_kernel<DT, NP, NKB, rq, nw>;
     if (!launch) {
-        hipError_t e = hipFuncSetAttribute((const void *)ks, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)LOOP_LDS_MAX);
-        if (e != hipSuccess) return e;
-        return hipFuncSetAttribute((const void *)kl, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LOOP_LDS_MAX);
+        for (const void *k : {(const void *)ks, (const void *)kl, (const void *)kt}) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LOOP_LDS_MAX);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
+    const void *kf = which == 0 ? (const void *)ks : which == 1 ? (const void *)kl : (const void *)kt;
     int dev = 0, ncu = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, which == 0 ? (const void *)ks : (const void *)kl,
-                                                         nw * 64, lds);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kf, nw * 64, lds);
     if (e != hipSuccess) return e;
     if (per_cu < 1 || ncu < 1) return hipErrorInvalidConfiguration;
     const unsigned grid =
         (unsigned)std::max<long long>(1, capped_grid(std::min<long long>(ntask, (long long)per_cu * ncu)));
     if (which == 0) {
         hipLaunchKernelGGL(ks, dim3(grid), dim3(nw * 64), lds, s, *a, h);
+        return hipGetLastError();
+    }
+    if (which == 2) {
+        hipLaunchKernelGGL(kt, dim3(grid), dim3(nw * 64), lds, s, *a, h);
         return hipGetLastError();
     }
     void *args[] = {(void *)a, (void *)&h};
@@ -461,7 +467,7 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
     // the Euclidean metric needs each map on both sides (query and reference rows differ)
     p->o_r1b = p->f.l2 ? b.take((size_t)B * p->N1 * p->f.ld * p->f.esz) : 0;
     p->o_r2b = p->f.l2 ? b.take((size_t)B * p->N2 * p->f.ld * p->f.esz) : 0;
-    p->o_ctl = b.take(256);
+    p->o_ctl = b.take(1024);    // control words 128 B apart: barrier, error, tail ticket / done / ready
     p->o_uprev = b.take(kb); p->o_uiter = b.take(kb);
     p->o_marks = p->explicit_starts ? b.take((size_t)p->N1 * 4) : 0;
     p->total = b.off;
@@ -519,12 +525,39 @@ void frm_dir_args(const FrmPlan &P, const void *m1q, const void *m1r, const void
 // Polls per grid-barrier wait of the loop kernel (a test aid lowers it to force the failure path).
 std::atomic<int> &loop_spin_limit() { static std::atomic<int> n{kSpinLimit}; return n; }
 
-// Half-steps [0, h_loop) run as one sweep and one update launch each, the
-// rest (all of them in the loop mode) in one cooperative loop kernel that
-// stops when no seed is active. The whole sequence can be captured into a graph.
+// How the half-steps of one FRM call are launched: [0, h_split) as one sweep
+// and one update launch each, the rest in one loop kernel (tail = 1,
+// cooperative) or one tail kernel (tail = 2); both stop when no seed is active.
+struct FrmExec {
+    int h_split, tail;
+};
+
+// Iterations run per half-step before the tail kernel takes over
+// (DDM_FRM_TAIL); -1 chooses by the work of one full sweep.
+std::atomic<int> &tail_after() { static std::atomic<int> n{-1}; return n; }
+
+// Launch plan of a call in the effective mode `mode` (the caller has already
+// replaced the loop mode where the device has no cooperative launches).
+// Automatic split: kernel boundaries cost less than the tail kernel's
+// completion counters and waits while a half-step has much work, so large
+// problems run the first three iterations (which hold nearly all the work on
+// shifted or moderately distorted pairs) per half-step; small ones hand over
+// after one, where launch overheads dominate.
+FrmExec frm_exec(int mode, const FrmPlan &P) {
+    if (mode == DDM_FRM_LOOP) return {0, 1};
+    if (mode == DDM_FRM_TAIL) {
+        int it = tail_after().load();
+        if (it < 0) it = (long long)P.B * P.k * P.N2 <= (1LL << 27) ? 1 : 3;
+        return {std::min(P.nhalf, 2 * it), 2};
+    }
+    return {P.nhalf, 0};
+}
+
+// Half-steps per E (all of them per half-step when E.h_split >= nhalf). The
+// whole sequence can be captured into a graph.
 int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, int32_t *out_i, int32_t *out_j,
             float *out_score, int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
-            void *ws, hipStream_t s, int h_loop) {
+            void *ws, hipStream_t s, FrmExec E) {
     unsigned char *w = (unsigned char *)ws;
     const MapFmt &f = P.f;
     const void *m1, *m2, *m1r, *m2r;
@@ -577,18 +610,21 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
         fa.st = st; fa.B = P.B; fa.nhalf = P.nhalf; fa.k = P.k; fa.qblocks = P.qblocks;
         fa.nch[0] = P.nch2; fa.nch[1] = P.nch1;
         fa.bar = ctl; fa.err = (int32_t *)(ctl + 32); fa.spin_limit = loop_spin_limit().load();
+        fa.tail = ctl + 64;
         const long long sweep_tasks = (long long)P.B * P.qblocks * std::max(P.nch1, P.nch2);
         const long long upd_tasks = (long long)P.B * ((P.k + 15) / 16);
-        for (int h = 0; h < std::min(h_loop, P.nhalf); ++h) {
+        const int h_split = std::max(0, std::min(E.h_split, P.nhalf));
+        for (int h = 0; h < h_split; ++h) {
             DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, 0, &fa, h, P.loop_lds, sweep_tasks, s, true); }));
             DDM_DT_SWITCH(f.dtype, frm_update_kernel, dim3((unsigned)capped_grid(std::min<long long>(upd_tasks, 2048))),
                           dim3(256), 0, s, fa, h);
             DDM_CHECK_LAUNCH();
         }
-        if (h_loop < P.nhalf) {
+        if (h_split < P.nhalf) {
             const int qb = nw_for(f.dtype) * 64 / 16;
             const long long ntask = std::max(sweep_tasks, (long long)P.B * ((P.k + qb - 1) / qb));
-            DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, 1, &fa, h_loop, P.loop_lds, ntask, s, true); }));
+            const int which = E.tail == 2 ? 2 : 1;
+            DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, which, &fa, h_split, P.loop_lds, ntask, s, true); }));
         }
     }
     const int col_blocks = (int)std::min<long long>((std::max(P.k, 1) + 255) / 256, 4096);
@@ -657,7 +693,7 @@ int c2f_plan(int H1, int W1, int H2, int W2, int d, int dtype, int factor, int c
 }
 
 int c2f_run(const C2fPlan &P, const void *F1, const void *F2, int32_t *out_i, int32_t *out_j, float *out_score,
-            int32_t capacity, int32_t *out_count, int32_t *crop_info, void *ws, hipStream_t s, int h_loop_mode) {
+            int32_t capacity, int32_t *out_count, int32_t *crop_info, void *ws, hipStream_t s, int mode) {
     unsigned char *w = (unsigned char *)ws;
     const CropGeom g = P.geom();
     // coarse maps and coarse FRM
@@ -670,7 +706,7 @@ int c2f_run(const C2fPlan &P, const void *F1, const void *F2, int32_t *out_i, in
     DDM_CHECK_LAUNCH();
     int32_t *ci = (int32_t *)(w + P.o_ci), *cj = (int32_t *)(w + P.o_cj), *cc = (int32_t *)(w + P.o_cc);
     int rc = frm_run(P.pc, FrmOpts{}, w + P.o_c1, w + P.o_c2, ci, cj, (float *)(w + P.o_cs), P.kc, cc, nullptr,
-                     nullptr, w + P.o_cws, s, h_loop_mode ? 0 : P.pc.nhalf);
+                     nullptr, w + P.o_cws, s, frm_exec(mode, P.pc));
     if (rc) return rc;
     // crop windows, crop batches, fine FRM
     int32_t *info = crop_info ? crop_info : (int32_t *)(w + P.o_info);
@@ -686,7 +722,7 @@ int c2f_run(const C2fPlan &P, const void *F1, const void *F2, int32_t *out_i, in
     int32_t *fi = (int32_t *)(w + P.o_fi), *fj = (int32_t *)(w + P.o_fj), *fc = (int32_t *)(w + P.o_fc);
     float *fsc = (float *)(w + P.o_fs);
     rc = frm_run(P.pf, FrmOpts{}, w + P.o_b1, w + P.o_b2, fi, fj, fsc, P.kf, fc, nullptr, nullptr, w + P.o_fws, s,
-                 h_loop_mode ? 0 : P.pf.nhalf);
+                 frm_exec(mode, P.pf));
     if (rc) return rc;
     // merge into full resolution, first tile wins, ordered output
     const int n1 = P.H1 * P.W1;
@@ -751,7 +787,7 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p,
 }
 
 // ------------------------------------------------------------- FRM mode
-std::atomic<int> &frm_mode() { static std::atomic<int> m{DDM_FRM_PER_HALF_STEP}; return m; }
+std::atomic<int> &frm_mode() { static std::atomic<int> m{DDM_FRM_TAIL}; return m; }
 
 bool cooperative_ok(int dev) {
     static std::mutex mu;
@@ -763,6 +799,12 @@ bool cooperative_ok(int dev) {
         known[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && v) ? 1 : 2;
     }
     return known[dev] == 1;
+}
+
+// The process-wide mode as it applies on device dev.
+int effective_mode(int dev) {
+    const int m = frm_mode().load();
+    return (m == DDM_FRM_LOOP && !cooperative_ok(dev)) ? DDM_FRM_PER_HALF_STEP : m;
 }
 
 // ---------------------------------------------------------- graph replay
@@ -838,8 +880,14 @@ const char *ddm_status_str(int status) {
 int64_t ddm_seed_count(int H, int W, int grid_stride) { return seed_count(H, W, grid_stride); }
 
 int ddm_frm_set_mode(int mode) {
-    if (mode != DDM_FRM_PER_HALF_STEP && mode != DDM_FRM_LOOP) return DDM_ERR_INVALID;
+    if (mode != DDM_FRM_PER_HALF_STEP && mode != DDM_FRM_LOOP && mode != DDM_FRM_TAIL) return DDM_ERR_INVALID;
     frm_mode().store(mode);
+    return DDM_OK;
+}
+
+int ddm_frm_set_tail_after(int iterations) {
+    if (iterations < -1 || iterations > DDM_MAX_ITER) return DDM_ERR_INVALID;
+    tail_after().store(iterations);
     return DDM_OK;
 }
 
@@ -969,19 +1017,21 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
     if (hipGetDevice(&dev) != hipSuccess) return DDM_ERR_HIP;
     uint64_t tol_bits;
     std::memcpy(&tol_bits, &O.pixel_tol, sizeof(tol_bits));
-    const int h_loop = (frm_mode() == DDM_FRM_LOOP && cooperative_ok(dev)) ? 0 : P.nhalf;
+    const FrmExec E = frm_exec(effective_mode(dev), P);
     const GraphKey key = {(uint64_t)dev, (uint64_t)B, (uint64_t)(uintptr_t)D1, (uint64_t)H1, (uint64_t)W1,
                           (uint64_t)(uintptr_t)D2, (uint64_t)H2, (uint64_t)W2, (uint64_t)d, (uint64_t)dtype,
                           (uint64_t)grid_stride, (uint64_t)max_iter, (uint64_t)(uintptr_t)out_i,
                           (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)seed_state,
-                          (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace, (uint64_t)h_loop,
+                          (uint64_t)(uintptr_t)query_counts, (uint64_t)(uintptr_t)workspace,
+                          (uint64_t)(uint32_t)E.h_split | ((uint64_t)E.tail << 32),
                           (uint64_t)(uintptr_t)O.starts, (uint64_t)(uint32_t)O.n_starts, tol_bits,
                           (uint64_t)(uintptr_t)O.basin, (uint64_t)metric,
-                          (uint64_t)(h_loop == 0 ? loop_spin_limit().load() : 0), (uint64_t)frm_grid_cap().load()};
+                          (uint64_t)(E.h_split < P.nhalf ? loop_spin_limit().load() : 0),
+                          (uint64_t)frm_grid_cap().load()};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return frm_run(P, O, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts,
-                       workspace, s, h_loop);
+                       workspace, s, E);
     });
 }
 
@@ -1049,17 +1099,18 @@ int ddm_c2f_match(const void *F1, int H1, int W1, const void *F2, int H2, int W2
     if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DDM_ERR_HIP;
-    const int loop = (frm_mode() == DDM_FRM_LOOP && cooperative_ok(dev)) ? 1 : 0;
+    const int mode = effective_mode(dev);
     const GraphKey key = {(uint64_t)dev, 0xC2F, (uint64_t)(uintptr_t)F1, (uint64_t)H1, (uint64_t)W1,
                           (uint64_t)(uintptr_t)F2, (uint64_t)H2, (uint64_t)W2, (uint64_t)d, (uint64_t)dtype,
                           (uint64_t)factor, (uint64_t)coarse_stride, (uint64_t)coarse_iter, (uint64_t)crop_h,
                           (uint64_t)crop_w, (uint64_t)fine_stride, (uint64_t)fine_iter, (uint64_t)(uintptr_t)out_i,
                           (uint64_t)(uintptr_t)out_j, (uint64_t)(uintptr_t)out_score, (uint64_t)capacity,
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)crop_info,
-                          (uint64_t)(uintptr_t)workspace, (uint64_t)loop,
-                          (uint64_t)(loop ? loop_spin_limit().load() : 0), (uint64_t)frm_grid_cap().load()};
+                          (uint64_t)(uintptr_t)workspace, (uint64_t)mode | ((uint64_t)(uint32_t)(tail_after().load() + 1) << 8),
+                          (uint64_t)(mode != DDM_FRM_PER_HALF_STEP ? loop_spin_limit().load() : 0),
+                          (uint64_t)frm_grid_cap().load()};
     return run_graphed(key, stream, [&](hipStream_t s) {
-        return c2f_run(P, F1, F2, out_i, out_j, out_score, capacity, out_count, crop_info, workspace, s, loop);
+        return c2f_run(P, F1, F2, out_i, out_j, out_score, capacity, out_count, crop_info, workspace, s, mode);
     });
 }
 

@@ -13,6 +13,12 @@
 // resident at once (cooperative launch), and each barrier wait is bounded:
 // past the bound the workgroup sets the error word and leaves the loop, so the
 // kernel always ends; the output count then reports the failure.
+//
+// The tail kernel runs half-steps h_begin.. in one plain launch without grid
+// barriers: workgroups take the tasks of all phases in one global order from a
+// ticket counter and wait only for tasks with earlier tickets, which
+// workgroups already running hold, so it needs no co-residency and ends as
+// soon as a half-step has no active seed.
 #pragma once
 #include "ddm_aux.hpp"
 
@@ -25,8 +31,9 @@ struct FrmArgs {
     int B, nhalf, k, qblocks;
     int nch[2];
     uint32_t *bar;        // loop kernel: barrier arrivals, zero at launch
-    int32_t *err;         // loop kernel: set to 1 when a barrier wait ran past its bound
-    int spin_limit;       // loop kernel: polls per barrier wait before giving up
+    int32_t *err;         // loop and tail kernels: set to 1 when a wait ran past its bound
+    int spin_limit;       // loop and tail kernels: polls per wait before giving up
+    uint32_t *tail;       // tail kernel: ticket, done and ready words at +0, +32, +64, zero at launch
 };
 
 // Task t of a phase -> (pair, task within the pair), given the per-pair counts.
@@ -42,46 +49,83 @@ __device__ __forceinline__ int task_locate(int B, int t, Count count, int *pair)
     return t;
 }
 
+// Sweep arguments of half-step h: its direction, query list and counts.
+__device__ __forceinline__ SweepArgs frm_sweep_args(const FrmArgs &a, int h) {
+    SweepArgs p = a.sw[h & 1];
+    p.qrows = a.st.qrows[h & 1];
+    p.qcount = a.st.counts + h;
+    return p;
+}
+
+// Sweep tasks of pair pr at half-step h: reference chunks x query groups of
+// the runtime split (0 when the pair has no active query).
+template <int DT>
+__device__ __forceinline__ int frm_sweep_tasks(const FrmArgs &a, const SweepArgs &p, int h, int pr) {
+    constexpr int GROUP = TILE * group_tiles(DT);
+    const int nq = a.st.counts[pr * a.st.cnt_bs + h];
+    if (nq <= 0) return 0;
+    const int nch = a.nch[h & 1];
+    const SplitGeom sg = split_geom(p.split, nq, p.split_rows, p.qblocks, p.chunk / GROUP, nch, p.rowcap);
+    return nch * sg.need * sg.s;
+}
+
+template <int DT>
+__device__ __forceinline__ int frm_sweep_total(const FrmArgs &a, const SweepArgs &p, int h) {
+    int total = 0;
+    for (int pr = 0; pr < a.B; ++pr) total += frm_sweep_tasks<DT>(a, p, h, pr);
+    return total;
+}
+
+// Sweep task t (over all pairs) of half-step h.
+template <int DT, int NP, int NKB, int RQ, int NW>
+__device__ __forceinline__ void frm_sweep_run(const FrmArgs &a, const SweepArgs &p, int h, int t,
+                                              unsigned char *lds) {
+    int pr;
+    const int tt = task_locate(a.B, t, [&](int q) { return frm_sweep_tasks<DT>(a, p, h, q); }, &pr);
+    const int nch = a.nch[h & 1];
+    sweep_task<DT, NP, NKB, RQ, NW, false>(p, pr, tt % nch, tt / nch, lds);
+}
+
 // Sweep phase of half-step h over the workgroups of the grid.
 template <int DT, int NP, int NKB, int RQ, int NW>
 __device__ __forceinline__ void frm_sweep_phase(const FrmArgs &a, int h, unsigned char *lds) {
-    constexpr int GROUP = TILE * group_tiles(DT);
-    const int dir = h & 1;
-    const int32_t *cnt = a.st.counts + h;
-    SweepArgs p = a.sw[dir];
-    p.qrows = a.st.qrows[h & 1];
-    p.qcount = cnt;
-    const int nch = a.nch[dir];
-    auto tasks = [&](int pr) {
-        const int nq = cnt[pr * a.st.cnt_bs];
-        if (nq <= 0) return 0;
-        const SplitGeom sg = split_geom(p.split, nq, p.split_rows, p.qblocks, p.chunk / GROUP, nch, p.rowcap);
-        return nch * sg.need * sg.s;
-    };
-    int total = 0;
-    for (int pr = 0; pr < a.B; ++pr) total += tasks(pr);
+    const SweepArgs p = frm_sweep_args(a, h);
+    const int total = frm_sweep_total<DT>(a, p, h);
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        int pr;
-        const int tt = task_locate(a.B, t, tasks, &pr);
         __syncthreads();                       // the previous task's waves are done with the LDS
-        sweep_task<DT, NP, NKB, RQ, NW, false>(p, pr, tt % nch, tt / nch, lds);
+        frm_sweep_run<DT, NP, NKB, RQ, NW>(a, p, h, t, lds);
     }
 }
 
-// Update phase of half-step h: NT threads per workgroup, NT/16 queries per task.
+// Update tasks of pair pr at half-step h: blocks of QB active queries.
+template <int QB>
+__device__ __forceinline__ int frm_update_tasks(const FrmArgs &a, int h, int pr) {
+    return (a.st.counts[pr * a.st.cnt_bs + h] + QB - 1) / QB;
+}
+
+template <int QB>
+__device__ __forceinline__ int frm_update_total(const FrmArgs &a, int h) {
+    int total = 0;
+    for (int pr = 0; pr < a.B; ++pr) total += frm_update_tasks<QB>(a, h, pr);
+    return total;
+}
+
+// Update task t (over all pairs) of half-step h with NT threads, NT/16 queries.
+template <int DT, int NT>
+__device__ __forceinline__ void frm_update_run(const FrmArgs &a, int h, int t, uint64_t *red) {
+    constexpr int QB = NT / 16;
+    int pr;
+    const int blk = task_locate(a.B, t, [&](int q) { return frm_update_tasks<QB>(a, h, q); }, &pr);
+    frm_update_task<DT, QB, NT>(a.rs[h & 1], a.st, h, h & 1, h / 2 + 1, pr, blk, red);
+}
+
+// Update phase of half-step h over the workgroups of the grid.
 template <int DT, int NT>
 __device__ __forceinline__ void frm_update_phase(const FrmArgs &a, int h, uint64_t *red) {
-    constexpr int QB = NT / 16;
-    const int dir = h & 1;
-    const int32_t *cnt = a.st.counts + h;
-    auto tasks = [&](int pr) { return (cnt[pr * a.st.cnt_bs] + QB - 1) / QB; };
-    int total = 0;
-    for (int pr = 0; pr < a.B; ++pr) total += tasks(pr);
+    const int total = frm_update_total<NT / 16>(a, h);
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        int pr;
-        const int blk = task_locate(a.B, t, tasks, &pr);
         __syncthreads();
-        frm_update_task<DT, QB, NT>(a.rs[dir], a.st, h, dir, h / 2 + 1, pr, blk, red);
+        frm_update_run<DT, NT>(a, h, t, red);
     }
 }
 
@@ -141,6 +185,90 @@ __global__ void __launch_bounds__(NW * 64) frm_loop_kernel(FrmArgs a, int h_begi
         frm_update_phase<DT, NW * 64>(a, h, reinterpret_cast<uint64_t *>(lds));
         target += gridDim.x;
         if (!grid_sync(a.bar, target, a.err, a.spin_limit, &flag)) return;
+    }
+}
+
+// Bounded wait of the tail kernel until *w >= target: thread 0 polls, the
+// workgroup follows, with agent-scope acquire after the wait. False, uniformly
+// over the workgroup, when the bound ran out here or another workgroup already
+// reported a timeout.
+__device__ __forceinline__ bool tail_wait(const uint32_t *w, uint32_t target, int32_t *err, int spin_limit,
+                                          int *flag) {
+    __syncthreads();                           // every wave has read the previous flag
+    if (threadIdx.x == 0) {
+        int ok = 1, spins = 0;
+        while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++spins > spin_limit) {
+                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+            if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *flag = ok;
+    }
+    __syncthreads();
+    return *flag != 0;
+}
+
+// Half-steps h_begin.. until one has no active seed, in one plain launch.
+// Tickets order the tasks: the sweep tasks of half-step h, then its update
+// tasks, then those of h + 1. Every workgroup walks the same sequence of
+// half-steps and derives each one's task counts from the active counts, so
+// all agree on where a ticket falls. An update task first waits until the
+// done counter covers every sweep task of its half-step (no later task can
+// finish before that); the workgroup finishing the last update task of h
+// publishes h + 1 through the ready word, after which its active counts are
+// final. A wait therefore only ever depends on tickets handed out earlier,
+// to workgroups already running: any grid completes, down to one workgroup.
+template <int DT, int NP, int NKB, int RQ, int NW>
+__global__ void __launch_bounds__(NW * 64) frm_tail_kernel(FrmArgs a, int h_begin) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    __shared__ int flag;
+    __shared__ uint32_t tk;
+    constexpr int QB = NW * 64 / 16;
+    uint32_t *ticket = a.tail, *done = a.tail + 32, *ready = a.tail + 64;
+    int h = h_begin;
+    if (h >= a.nhalf) return;
+    SweepArgs p = frm_sweep_args(a, h);
+    uint32_t sb = 0;                                           // first ticket of half-step h
+    uint32_t ns = frm_sweep_total<DT>(a, p, h), nu = frm_update_total<QB>(a, h);
+    if (ns == 0) return;
+    for (;;) {
+        __syncthreads();                                       // the LDS and tk are free again
+        if (threadIdx.x == 0) tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint32_t t = tk;
+        while (t >= sb + ns + nu) {                            // past half-step h: wait until h + 1 is known
+            if (!tail_wait(ready, (uint32_t)(h + 1 - h_begin), a.err, a.spin_limit, &flag)) return;
+            sb += ns + nu;
+            if (++h >= a.nhalf) return;
+            p = frm_sweep_args(a, h);
+            ns = frm_sweep_total<DT>(a, p, h);
+            if (ns == 0) return;
+            nu = frm_update_total<QB>(a, h);
+        }
+        const bool upd = t >= sb + ns;
+        if (upd) {
+            if (!tail_wait(done, sb + ns, a.err, a.spin_limit, &flag)) return;
+            frm_update_run<DT, NW * 64>(a, h, (int)(t - sb - ns), reinterpret_cast<uint64_t *>(lds));
+        } else {
+            frm_sweep_run<DT, NP, NKB, RQ, NW>(a, p, h, (int)(t - sb), lds);
+        }
+        __syncthreads();                                       // every wave's writes of the task are issued
+        if (threadIdx.x == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (upd && prev + 1 == sb + ns + nu) {             // last task of half-step h
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+                __hip_atomic_store(ready, (uint32_t)(h + 1 - h_begin), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 

@@ -168,7 +168,7 @@ int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* How FRM calls are executed (process-wide; results are identical):
- *   DDM_FRM_PER_HALF_STEP (default): a sweep and an update launch for every
+ *   DDM_FRM_PER_HALF_STEP: a sweep and an update launch for every
  *     half-step of all max_iter iterations. Both kernels stride over the
  *     active work only, so the half-steps after convergence cost a few
  *     microseconds each.
@@ -177,20 +177,33 @@ int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
  *     (the device must support cooperative launches, else per half-step).
  *     Its barriers cost more than kernel boundaries on large maps; it pays off
  *     on small ones.
+ *   DDM_FRM_TAIL (default): the first iterations per half-step (see
+ *     ddm_frm_set_tail_after), the rest in one plain kernel launch whose
+ *     workgroups take the remaining tasks in a global order from a ticket
+ *     counter and stop as soon as no seed is active, so the iterations after
+ *     convergence cost nothing. No co-residency is needed: a workgroup only
+ *     waits for tasks handed out before its own. Its waits are bounded like
+ *     the loop kernel's barriers (out_count = -1 past the bound).
  * The launch sequence of a call is recorded once into a HIP graph, cached under
  * the call's argument values and the mode, and replayed; on a stream that is
  * being captured it is recorded into the caller's graph.
  * ddm_frm_set_mode returns DDM_ERR_INVALID for other values. */
-typedef enum { DDM_FRM_PER_HALF_STEP = 0, DDM_FRM_LOOP = 1 } ddm_frm_mode;
+typedef enum { DDM_FRM_PER_HALF_STEP = 0, DDM_FRM_LOOP = 1, DDM_FRM_TAIL = 2 } ddm_frm_mode;
 int ddm_frm_set_mode(int mode);
 int ddm_frm_get_mode(void);
-/* Test aid for the failure path of DDM_FRM_LOOP: the number of polls a grid-barrier wait makes
- * before giving up (0 restores the default of 2^20, about 1 s). A tiny value makes the barriers
- * time out on purpose; the kernel still ends and out_count reads -1. Process-wide; graph-cached
- * calls keep the value they were recorded with. */
+/* Iterations run per half-step before the tail kernel takes over in DDM_FRM_TAIL (0..DDM_MAX_ITER;
+ * 0 runs every half-step in the tail kernel). -1 (the default) chooses by size: one iteration when
+ * pairs x seeds x image-2 pixels <= 2^27, else three. Process-wide; DDM_ERR_INVALID outside
+ * -1..DDM_MAX_ITER. */
+int ddm_frm_set_tail_after(int iterations);
+/* Test aid for the failure path of DDM_FRM_LOOP and DDM_FRM_TAIL: the number of polls a wait makes
+ * before giving up (0 restores the default of 2^20, about 1 s). A tiny value makes the loop
+ * kernel's barriers time out on purpose (and any tail-kernel wait that does not end at once); the
+ * kernel still ends and out_count reads -1. Process-wide; graph-cached calls keep the value they
+ * were recorded with. */
 int ddm_frm_set_barrier_polls(int polls);
-/* Test aid against races between workgroups: caps the grid of the FRM sweep, update and loop
- * kernels (which stride their tasks over whatever grid they get) at max_workgroups; 0 removes
+/* Test aid against races between workgroups: caps the grid of the FRM sweep, update, loop and
+ * tail kernels (which spread their tasks over whatever grid they get) at max_workgroups; 0 removes
  * the cap. Outputs must be bit-identical with any cap; 1 runs every task in one workgroup.
  * Process-wide; graph-cached calls keep the value they were recorded with. */
 int ddm_debug_set_grid_cap(int max_workgroups);

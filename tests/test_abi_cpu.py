@@ -34,11 +34,19 @@ def test_header_symbols_exported(L):
 
 
 def test_frm_mode_switch(L):
-    assert L.ddm_frm_get_mode() == 0                 # per half-step by default
+    assert L.ddm_frm_get_mode() == 2                 # first iterations per half-step, then the tail kernel
     assert L.ddm_frm_set_mode(1) == 0 and L.ddm_frm_get_mode() == 1
-    assert L.ddm_frm_set_mode(2) == -1 and L.ddm_frm_set_mode(-1) == -1
-    assert L.ddm_frm_get_mode() == 1                 # a rejected value changes nothing
     assert L.ddm_frm_set_mode(0) == 0 and L.ddm_frm_get_mode() == 0
+    assert L.ddm_frm_set_mode(3) == -1 and L.ddm_frm_set_mode(-1) == -1
+    assert L.ddm_frm_get_mode() == 0                 # a rejected value changes nothing
+    assert L.ddm_frm_set_mode(2) == 0 and L.ddm_frm_get_mode() == 2
+
+
+def test_tail_after_setter(L):
+    assert L.ddm_frm_set_tail_after(-2) == -1
+    assert L.ddm_frm_set_tail_after(65) == -1        # beyond DDM_MAX_ITER
+    for n in (0, 64, 2, -1):                         # -1: automatic (the default)
+        assert L.ddm_frm_set_tail_after(n) == 0
 
 
 def test_grid_cap_setter(L):

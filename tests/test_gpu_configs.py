@@ -198,7 +198,7 @@ def test_frm_graph_replays_match_direct_launches(ddm):
             del x
     finally:
         ddm.profile_enable(0)
-        ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
+        ddm.frm_set_mode(ddm.FRM_DEFAULT)
 
 
 FRM_MODE_CASES = [
@@ -213,12 +213,24 @@ FRM_MODE_CASES = [
 ]
 
 
+def _set_exec(ddm, mode, tail_after=-1):
+    ddm.frm_set_mode(mode)
+    ddm.frm_set_tail_after(tail_after)
+
+
+# (mode, iterations before the tail kernel, sweep timing on = direct launches)
+MODE_RUNS = ((0, 2, True), (0, 2, False), (0, 2, False), (1, 2, False), (1, 2, False), (1, 2, True),
+             (2, 2, False), (2, 2, False), (2, 2, True), (2, 0, False), (2, 1, False), (2, 3, False),
+             (2, -1, False), (2, -1, True))
+
+
 @pytest.mark.parametrize("name,S,it,batched", FRM_MODE_CASES)
 def test_frm_modes_agree(ddm, name, S, it, batched):
-    """Per-half-step launches and the loop kernel give the same bits: pairs,
-    scores, per-seed states and query counts; repeated calls on one workspace
-    agree too (the barrier counter restarts every call), and so do direct
-    launches (sweep timing on) and graph replays."""
+    """Per-half-step launches, the loop kernel and the tail kernel (taking over
+    after 0 to 3 iterations) give the same bits: pairs, scores, per-seed states
+    and query counts; repeated calls on one workspace agree too (the barrier and
+    ticket counters restart every call), and so do direct launches (sweep timing
+    on) and graph replays."""
     import torch
     pairs = synth.make_config(name)
     D1 = torch.stack([dev(p.D1, p.dtype) for p in pairs]); D2 = torch.stack([dev(p.D2, p.dtype) for p in pairs])
@@ -228,19 +240,17 @@ def test_frm_modes_agree(ddm, name, S, it, batched):
     buf = ddm.FrmBuffers(len(pairs), p0.H1, p0.W1, p0.H2, p0.W2, p0.d, D1.dtype, S, it, D1.device)
     runs = []
     try:
-        for mode, timed in ((ddm.FRM_PER_HALF_STEP, True), (ddm.FRM_PER_HALF_STEP, False),
-                            (ddm.FRM_PER_HALF_STEP, False), (ddm.FRM_LOOP, False), (ddm.FRM_LOOP, False),
-                            (ddm.FRM_LOOP, True)):
-            ddm.frm_set_mode(mode)
+        for mode, after, timed in MODE_RUNS:
+            _set_exec(ddm, mode, after)
             ddm.profile_enable(2 if timed else 0)
             buf.count.fill_(-3); buf.qcounts.fill_(-3); buf.state.fill_(-3)
             ddm.frm_match_into(D1, D2, S, it, buf, batched=batched)
             torch.cuda.synchronize()
             ddm.profile_read()
-            runs.append(((mode, timed), _frm_outputs(buf)))
+            runs.append(((mode, after, timed), _frm_outputs(buf)))
     finally:
         ddm.profile_enable(0)
-        ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
+        _set_exec(ddm, ddm.FRM_DEFAULT)
     ref = runs[0][1]
     for what, r in runs[1:]:
         _assert_same(r, ref, f"{name} {what}")
@@ -259,9 +269,10 @@ GRID_CAP_CASES = [
 
 @pytest.mark.parametrize("case", range(len(GRID_CAP_CASES)))
 def test_frm_grid_cap_does_not_change_results(ddm, case):
-    """The FRM phase kernels stride their tasks over the grid they get; with the grid capped at
-    1, a few or many workgroups, in both execution modes, every output is bit-identical (no
-    dependence on how tasks spread over concurrent workgroups)."""
+    """The FRM phase kernels spread their tasks over the grid they get; with the grid capped at
+    1, a few or many workgroups, in every execution mode (the tail kernel taking over after 0 or
+    2 iterations), every output is bit-identical (no dependence on how tasks spread over
+    concurrent workgroups)."""
     import torch
     make, S, it, batched, caps = GRID_CAP_CASES[case]
     pairs = make()
@@ -272,8 +283,8 @@ def test_frm_grid_cap_does_not_change_results(ddm, case):
     buf = ddm.FrmBuffers(len(pairs), p0.H1, p0.W1, p0.H2, p0.W2, p0.d, D1.dtype, S, it, D1.device)
     ref = None
     try:
-        for mode in (ddm.FRM_PER_HALF_STEP, ddm.FRM_LOOP):
-            ddm.frm_set_mode(mode)
+        for mode, after in ((ddm.FRM_PER_HALF_STEP, 2), (ddm.FRM_LOOP, 2), (ddm.FRM_TAIL, 0), (ddm.FRM_TAIL, 2)):
+            _set_exec(ddm, mode, after)
             for cap in (0,) + tuple(caps):
                 ddm.debug_set_grid_cap(cap)
                 buf.count.fill_(-3); buf.qcounts.fill_(-3); buf.state.fill_(-3)
@@ -282,7 +293,7 @@ def test_frm_grid_cap_does_not_change_results(ddm, case):
                 if ref is None:
                     ref = got
                 else:
-                    _assert_same(got, ref, f"mode {mode} cap {cap}")
+                    _assert_same(got, ref, f"mode {mode} after {after} cap {cap}")
     finally:
         ddm.debug_set_grid_cap(0)
-        ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
+        _set_exec(ddm, ddm.FRM_DEFAULT)

@@ -155,20 +155,24 @@ def test_invalid_starts_are_ignored_and_empty_lists(ddm):
         assert torch.equal(x, y)
 
 
-def test_options_in_loop_mode_equal_per_half_step(ddm):
+def test_options_in_loop_and_tail_modes_equal_per_half_step(ddm):
     import torch
     (p,) = synth.make_config("frm_512x384x24_f16")
     D1, D2 = dev(p.D1, p.dtype), dev(p.D2, p.dtype)
     starts = torch.tensor(np.random.default_rng(5).integers(0, p.H1 * p.W1, 2500), device="cuda")
     runs = []
     try:
-        for mode in (ddm.FRM_PER_HALF_STEP, ddm.FRM_LOOP):
+        for mode, after in ((ddm.FRM_PER_HALF_STEP, 2), (ddm.FRM_LOOP, 2), (ddm.FRM_TAIL, 2), (ddm.FRM_TAIL, 0)):
             ddm.frm_set_mode(mode)
+            ddm.frm_set_tail_after(after)
             runs.append(ddm.frm_match_ex(D1, D2, starts=starts, max_iter=5, pixel_tol=2.0, ret_basin=True,
                                          return_state=True))
     finally:
-        ddm.frm_set_mode(ddm.FRM_PER_HALF_STEP)
-    a, b = runs
-    for x, y in zip(a[:4], b[:4]):
-        assert torch.equal(x, y)
-    assert torch.equal(a[-1]["state"], b[-1]["state"]) and torch.equal(a[-1]["query_counts"], b[-1]["query_counts"])
+        ddm.frm_set_mode(ddm.FRM_DEFAULT)
+        ddm.frm_set_tail_after(-1)
+    a = runs[0]
+    for b in runs[1:]:
+        for x, y in zip(a[:4], b[:4]):
+            assert torch.equal(x, y)
+        assert torch.equal(a[-1]["state"], b[-1]["state"])
+        assert torch.equal(a[-1]["query_counts"], b[-1]["query_counts"])
