@@ -808,7 +808,7 @@ int effective_mode(int dev) {
 }
 
 // ---------------------------------------------------------- graph replay
-// An FRM call is ~4*max_iter small launches whose host-side enqueue cost
+// An FRM call is up to ~4*max_iter small launches whose host-side enqueue cost
 // exceeds their GPU time once the active set has shrunk. The sequence depends
 // only on the call's arguments, so it is captured once into a HIP graph on a
 // private capture stream, instantiated, cached (a few entries, most recently

@@ -1,5 +1,6 @@
-// ddm_frm.hpp -- the FRM iteration: sweep and update phases, run either as one
-// pair of launches per half-step or as one cooperative loop kernel.
+// ddm_frm.hpp -- the FRM iteration: sweep and update phases, run as one pair
+// of launches per half-step, as one cooperative loop kernel, or per half-step
+// for the first iterations and then as one tail kernel.
 //
 // Both phases enumerate only the active work of every pair (query blocks with
 // queries, times sub-chunks of the runtime split; query blocks of the update)
