@@ -73,6 +73,7 @@ def _declare(lib):
     lib.ddm_frm_set_tail_after.argtypes = [I]; lib.ddm_frm_set_tail_after.restype = I
     lib.ddm_frm_set_barrier_polls.argtypes = [I]; lib.ddm_frm_set_barrier_polls.restype = I
     lib.ddm_debug_set_grid_cap.argtypes = [I]; lib.ddm_debug_set_grid_cap.restype = I
+    lib.ddm_debug_set_output_bitmap_limit.argtypes = [I]; lib.ddm_debug_set_output_bitmap_limit.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
     lib.ddm_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]; lib.ddm_profile_read.restype = I
     return lib
@@ -165,6 +166,13 @@ def debug_set_grid_cap(max_workgroups: int):
     """Cap the grid of the FRM phase kernels (0: no cap); outputs must not change with it.
     A test aid against dependences between concurrent workgroups."""
     _rc(lib().ddm_debug_set_grid_cap(max_workgroups), "ddm_debug_set_grid_cap")
+
+
+def debug_set_output_bitmap_limit(max_pixels: int):
+    """Largest image 1 (pixels) whose FRM output is collected and ordered in one workgroup per pair
+    through an LDS bitmap (-1: the default 2^19; 0: always the multi-workgroup compaction).
+    A test aid: both paths must give identical outputs."""
+    _rc(lib().ddm_debug_set_output_bitmap_limit(max_pixels), "ddm_debug_set_output_bitmap_limit")
 
 
 def profile_enable(mask: int):
@@ -458,5 +466,5 @@ def mutual_nn(D1: torch.Tensor, D2: torch.Tensor, return_nn: bool = False, metri
 __all__ = ["nn", "frm_match", "frm_match_batched", "frm_match_into", "frm_match_ex", "c2f_match", "mutual_nn",
            "mutual_nn_into", "seed_count", "to_xy", "FrmBuffers", "MutualBuffers", "DDMError", "lib", "LIB_PATH",
            "profile_enable", "profile_read", "frm_set_mode", "frm_get_mode", "frm_set_barrier_polls",
-           "debug_set_grid_cap", "frm_set_tail_after",
+           "debug_set_grid_cap", "debug_set_output_bitmap_limit", "frm_set_tail_after",
            "FRM_PER_HALF_STEP", "FRM_LOOP", "FRM_TAIL", "FRM_DEFAULT", "METRICS"]

@@ -32,6 +32,7 @@ constexpr size_t LDS_MAX = 160 * 1024;
 constexpr long long MIN_WG = 256;          // one workgroup per CU
 constexpr size_t LOOP_LDS_MAX = LDS_MAX - 1024;   // the FRM loop kernel keeps a few LDS words of its own
 constexpr int MAX_PIX = 1 << 27;
+constexpr int OUT_MAX_PIXELS = 1 << 19;     // image-1 pixels of the one-workgroup FRM output (bitmap + ranks: 128 KB)
 
 struct MapFmt {
     int dtype, d;
@@ -243,6 +244,9 @@ hipError_t prepare_kernels() {
                         if (e != hipSuccess) status = e;
                     }
                 }
+        hipError_t e = hipFuncSetAttribute((const void *)frm_output_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(OUT_MAX_PIXELS / 4));
+        if (e != hipSuccess) status = e;
     });
     return status;
 }
@@ -522,6 +526,11 @@ void frm_dir_args(const FrmPlan &P, const void *m1q, const void *m1r, const void
     r->neg_out = f.l2 ? 1 : 0;
 }
 
+// Largest image-1 map (pixels) whose FRM output goes through the one-workgroup
+// bitmap kernel; larger maps (or a test aid lowering it) take the collection
+// kernel and the multi-workgroup compaction.
+std::atomic<int> &output_bitmap_limit() { static std::atomic<int> n{OUT_MAX_PIXELS}; return n; }
+
 // Polls per grid-barrier wait of the loop kernel (a test aid lowers it to force the failure path).
 std::atomic<int> &loop_spin_limit() { static std::atomic<int> n{kSpinLimit}; return n; }
 
@@ -626,6 +635,15 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
             const int which = E.tail == 2 ? 2 : 1;
             DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, which, &fa, h_split, P.loop_lds, ntask, s, true); }));
         }
+    }
+    if (P.N1 <= output_bitmap_limit().load() && P.k <= OUT_NT * OUT_SPT) {
+        // one workgroup per pair: collection and ordered output through an LDS bitmap
+        hipLaunchKernelGGL(frm_output_kernel, dim3(P.B), dim3(OUT_NT), (size_t)(P.N1 + 31) / 32 * 8, s, st, P.k,
+                           seed_state, (const int32_t *)st.counts, query_counts, P.nhalf, P.W1, O.pixel_tol,
+                           P.explicit_starts ? 1 : 0, P.N1, out_i, out_j, out_score, (long long)capacity, capacity,
+                           out_count, (const int32_t *)(ctl + 32));
+        DDM_CHECK_LAUNCH();
+        return DDM_OK;
     }
     const int col_blocks = (int)std::min<long long>((std::max(P.k, 1) + 255) / 256, 4096);
     hipLaunchKernelGGL(frm_collect_kernel, dim3(col_blocks, P.B), dim3(256), 0, s, st, P.k, seed_state,
@@ -893,6 +911,12 @@ int ddm_frm_set_tail_after(int iterations) {
 
 int ddm_frm_get_mode(void) { return frm_mode().load(); }
 
+int ddm_debug_set_output_bitmap_limit(int max_pixels) {
+    if (max_pixels < -1) return DDM_ERR_INVALID;
+    output_bitmap_limit().store(max_pixels < 0 ? OUT_MAX_PIXELS : std::min(max_pixels, OUT_MAX_PIXELS));
+    return DDM_OK;
+}
+
 int ddm_debug_set_grid_cap(int max_workgroups) {
     if (max_workgroups < 0) return DDM_ERR_INVALID;
     frm_grid_cap().store(max_workgroups);
@@ -1028,7 +1052,8 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
                           (uint64_t)(uintptr_t)O.starts, (uint64_t)(uint32_t)O.n_starts, tol_bits,
                           (uint64_t)(uintptr_t)O.basin, (uint64_t)metric,
                           (uint64_t)(E.h_split < P.nhalf ? loop_spin_limit().load() : 0),
-                          (uint64_t)frm_grid_cap().load()};
+                          (uint64_t)(uint32_t)frm_grid_cap().load() |
+                              ((uint64_t)(uint32_t)output_bitmap_limit().load() << 32)};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return frm_run(P, O, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts,
                        workspace, s, E);
@@ -1108,7 +1133,8 @@ int ddm_c2f_match(const void *F1, int H1, int W1, const void *F2, int H2, int W2
                           (uint64_t)(uintptr_t)out_count, (uint64_t)(uintptr_t)crop_info,
                           (uint64_t)(uintptr_t)workspace, (uint64_t)mode | ((uint64_t)(uint32_t)(tail_after().load() + 1) << 8),
                           (uint64_t)(mode != DDM_FRM_PER_HALF_STEP ? loop_spin_limit().load() : 0),
-                          (uint64_t)frm_grid_cap().load()};
+                          (uint64_t)(uint32_t)frm_grid_cap().load() |
+                              ((uint64_t)(uint32_t)output_bitmap_limit().load() << 32)};
     return run_graphed(key, stream, [&](hipStream_t s) {
         return c2f_run(P, F1, F2, out_i, out_j, out_score, capacity, out_count, crop_info, workspace, s, mode);
     });

@@ -400,6 +400,27 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
 // reported pixel u. pixel_tol > 0: kept = pixel distance |yx(u_old) - yx(u)|
 // below pixel_tol (in double, as a Euclidean distance), reported pixel u_old
 // when report_old (explicit starts), else u.
+// One seed's part of the collection: its state row (when asked for) and the
+// image-1 pixel it is kept at, or -1.
+__device__ __forceinline__ int frm_collect_seed(const FrmState &st, long long ko, int a, int32_t *ss, bool ran_last,
+                                                int max_iter, int W1, double pixel_tol, int report_old) {
+    const int u = st.u[ko + a], v = st.v[ko + a], it = st.conv[ko + a];
+    const int uold = (ran_last && st.uiter[ko + a] == max_iter) ? st.uprev[ko + a] : u;
+    bool kept;
+    int i = u;
+    if (pixel_tol > 0.0) {
+        const double dy = (double)(uold / W1 - u / W1), dx = (double)(uold % W1 - u % W1);
+        kept = sqrt(dy * dy + dx * dx) < pixel_tol;
+        if (report_old) i = uold;
+    } else {
+        kept = it >= 0;
+    }
+    if (ss) {
+        ss[0] = u; ss[1] = v; ss[2] = it; ss[3] = uold;
+    }
+    return kept ? i : -1;
+}
+
 __global__ void __launch_bounds__(256) frm_collect_kernel(FrmState st, int kcap, int32_t *seed_state,
                                                           const int32_t *counts_in, int32_t *query_counts,
                                                           int nhalf, int W1, double pixel_tol, int report_old) {
@@ -410,36 +431,132 @@ __global__ void __launch_bounds__(256) frm_collect_kernel(FrmState st, int kcap,
     const bool ran_last = cnt[nhalf - 2] > 0;      // forward queries of the last iteration
     const int max_iter = nhalf / 2;
     for (int a = blockIdx.x * 256 + threadIdx.x; a < kcap; a += gridDim.x * 256) {
+        int32_t *ss = seed_state ? seed_state + (pair * (long long)kcap + a) * 4 : nullptr;
         if (a >= k) {
-            if (seed_state) {
-                int32_t *ss = seed_state + (pair * (long long)kcap + a) * 4;
+            if (ss) {
                 ss[0] = -1; ss[1] = -1; ss[2] = -1; ss[3] = -1;
             }
             continue;
         }
-        const int u = st.u[ko + a], v = st.v[ko + a], it = st.conv[ko + a];
-        const int uold = (ran_last && st.uiter[ko + a] == max_iter) ? st.uprev[ko + a] : u;
-        bool kept;
-        int i = u;
-        if (pixel_tol > 0.0) {
-            const double dy = (double)(uold / W1 - u / W1), dx = (double)(uold % W1 - u % W1);
-            kept = sqrt(dy * dy + dx * dx) < pixel_tol;
-            if (report_old) i = uold;
-        } else {
-            kept = it >= 0;
-        }
-        if (kept) {
-            st.match_j[pair * st.n1_bs + i] = v;
+        const int i = frm_collect_seed(st, ko, a, ss, ran_last, max_iter, W1, pixel_tol, report_old);
+        if (i >= 0) {
+            st.match_j[pair * st.n1_bs + i] = st.v[ko + a];
             st.match_s[pair * st.n1_bs + i] = st.score[ko + a];
-        }
-        if (seed_state) {
-            int32_t *ss = seed_state + (pair * (long long)kcap + a) * 4;
-            ss[0] = u; ss[1] = v; ss[2] = it; ss[3] = uold;
         }
     }
     if (query_counts && blockIdx.x == 0)
         for (int h = threadIdx.x; h < nhalf; h += 256)
             query_counts[pair * (long long)nhalf + h] = counts_in[pair * st.cnt_bs + h];
+}
+
+// Collection and ordered output of a pair in one workgroup, for problems whose
+// image-1 pixels fit a bitmap in LDS and whose seeds fit the workgroup's
+// registers (OUT_SPT per thread). Each thread loads all its seeds at once and
+// keeps (pixel, j, score) of the kept ones; their pixels are marked in the
+// bitmap; an exclusive scan of the words' population counts, kept in LDS,
+// gives every marked pixel its rank, so each kept seed writes its pair straight
+// to out[rank] (seeds reporting the same pixel report the same pair and write
+// the same slot). The outputs equal those of frm_collect_kernel followed by
+// the dense compaction; out_count = -1 when *err is set.
+constexpr int OUT_NT = 1024, OUT_SPT = 4;   // up to 4096 seeds per pair (more: one workgroup falls behind)
+__global__ void __launch_bounds__(OUT_NT) frm_output_kernel(FrmState st, int kcap, int32_t *seed_state,
+                                                            const int32_t *counts_in, int32_t *query_counts,
+                                                            int nhalf, int W1, double pixel_tol, int report_old,
+                                                            int N1, int32_t *out_i, int32_t *out_j, float *out_s,
+                                                            long long out_bs, int capacity, int32_t *out_count,
+                                                            const int32_t *err) {
+    extern __shared__ uint32_t obits[];     // bitmap [nwords], then exclusive word ranks [nwords]
+    __shared__ int wsum[OUT_NT / 64];
+    const int pair = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nwords = (N1 + 31) >> 5;
+    uint32_t *bits = obits;
+    int *rank0 = reinterpret_cast<int *>(obits + nwords);
+    for (int q = tid; q < nwords; q += OUT_NT) bits[q] = 0u;
+    const long long ko = pair * st.k_bs;
+    const int32_t *cnt = counts_in + pair * st.cnt_bs;
+    const int k = min(cnt[0], kcap);
+    const bool ran_last = cnt[nhalf - 2] > 0;
+    const int max_iter = nhalf / 2;
+
+    // every load of this thread's seeds first, then the tests
+    int u[OUT_SPT], v[OUT_SPT], it[OUT_SPT], ui[OUT_SPT], up[OUT_SPT];
+    float sc[OUT_SPT];
+#pragma unroll
+    for (int r = 0; r < OUT_SPT; ++r) {
+        const int a = r * OUT_NT + tid;
+        if (a < k) {
+            u[r] = st.u[ko + a]; v[r] = st.v[ko + a]; it[r] = st.conv[ko + a]; sc[r] = st.score[ko + a];
+            ui[r] = st.uiter[ko + a]; up[r] = st.uprev[ko + a];
+        }
+    }
+    int pix[OUT_SPT];
+#pragma unroll
+    for (int r = 0; r < OUT_SPT; ++r) {
+        const int a = r * OUT_NT + tid;
+        pix[r] = -1;
+        if (a < k) {
+            const int uold = (ran_last && ui[r] == max_iter) ? up[r] : u[r];
+            bool kept;
+            int i = u[r];
+            if (pixel_tol > 0.0) {
+                const double dy = (double)(uold / W1 - u[r] / W1), dx = (double)(uold % W1 - u[r] % W1);
+                kept = sqrt(dy * dy + dx * dx) < pixel_tol;
+                if (report_old) i = uold;
+            } else {
+                kept = it[r] >= 0;
+            }
+            if (kept) pix[r] = i;
+            if (seed_state) {
+                int32_t *ss = seed_state + (pair * (long long)kcap + a) * 4;
+                ss[0] = u[r]; ss[1] = v[r]; ss[2] = it[r]; ss[3] = uold;
+            }
+        } else if (a < kcap && seed_state) {
+            int32_t *ss = seed_state + (pair * (long long)kcap + a) * 4;
+            ss[0] = -1; ss[1] = -1; ss[2] = -1; ss[3] = -1;
+        }
+    }
+    if (query_counts)
+        for (int h = tid; h < nhalf; h += OUT_NT) query_counts[pair * (long long)nhalf + h] = cnt[h];
+    __syncthreads();                           // the bitmap is clear
+#pragma unroll
+    for (int r = 0; r < OUT_SPT; ++r)
+        if (pix[r] >= 0) atomicOr(&bits[pix[r] >> 5], 1u << (pix[r] & 31));
+    __syncthreads();                           // the bitmap is complete
+
+    // exclusive rank of each word: thread t owns a run of words
+    const int per = (nwords + OUT_NT - 1) / OUT_NT;
+    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
+    int c = 0;
+    for (int q = w0; q < w1; ++q) c += __popc(bits[q]);
+    int incl = c;
+    for (int m = 1; m < 64; m <<= 1) {
+        const int o = __shfl_up(incl, m);
+        if (lane >= m) incl += o;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int base = incl - c, total = 0;
+    for (int q = 0; q < OUT_NT / 64; ++q) {
+        if (q < w) base += wsum[q];
+        total += wsum[q];
+    }
+    for (int q = w0; q < w1; ++q) {
+        rank0[q] = base;
+        base += __popc(bits[q]);
+    }
+    __syncthreads();                           // every word's rank is in place
+#pragma unroll
+    for (int r = 0; r < OUT_SPT; ++r) {
+        const int i = pix[r];
+        if (i >= 0) {
+            const int rank = rank0[i >> 5] + __popc(bits[i >> 5] & ((1u << (i & 31)) - 1u));
+            if (rank < capacity) {
+                const long long o = pair * out_bs + rank;
+                out_i[o] = i; out_j[o] = v[r]; out_s[o] = sc[r];
+            }
+        }
+    }
+    if (tid == 0) out_count[pair] = (err && *err) ? -1 : (total < capacity ? total : capacity);
 }
 
 // ---------------------------------------------------------------------------

@@ -207,6 +207,13 @@ int ddm_frm_set_barrier_polls(int polls);
  * the cap. Outputs must be bit-identical with any cap; 1 runs every task in one workgroup.
  * Process-wide; graph-cached calls keep the value they were recorded with. */
 int ddm_debug_set_grid_cap(int max_workgroups);
+/* Test aid for the two output paths of FRM: a call whose image 1 has at most max_pixels pixels (and
+ * at most 4096 seeds per pair) collects and orders its pairs in one workgroup per pair through a
+ * bitmap of image-1 pixels in LDS; larger ones use a collection kernel and a multi-workgroup
+ * compaction of a dense match array. Both give identical outputs. -1 restores the default (2^19,
+ * also the maximum); 0 sends every call down the multi-workgroup path. Process-wide;
+ * graph-cached calls keep the value they were recorded with. DDM_ERR_INVALID below -1. */
+int ddm_debug_set_output_bitmap_limit(int max_pixels);
 
 /* ----------------------------------------------------- coarse-to-fine ---
  * Matching of maps larger than the network's 512-px input ("MASt3R" note on cv-learn.com,

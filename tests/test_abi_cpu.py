@@ -55,6 +55,12 @@ def test_grid_cap_setter(L):
     assert L.ddm_debug_set_grid_cap(0) == 0
 
 
+def test_output_bitmap_limit_setter(L):
+    assert L.ddm_debug_set_output_bitmap_limit(-2) == -1
+    for n in (0, 1000, 1 << 30, -1):                 # above the maximum it is clamped; -1 = default
+        assert L.ddm_debug_set_output_bitmap_limit(n) == 0
+
+
 def test_barrier_polls_setter(L):
     assert L.ddm_frm_set_barrier_polls(-1) == -1
     assert L.ddm_frm_set_barrier_polls(3) == 0

@@ -297,3 +297,62 @@ def test_frm_grid_cap_does_not_change_results(ddm, case):
     finally:
         ddm.debug_set_grid_cap(0)
         _set_exec(ddm, ddm.FRM_DEFAULT)
+
+
+OUTPUT_PATH_CASES = [
+    ("tiny_frm_64x48x24_f32", 8, 10, False),
+    ("frm_512x384x24_f16", 8, 10, False),
+    ("frm_512x384x24_f16", 1000, 10, False),          # no seeds
+    ("batched_frm_16x512x384x24_f16", 8, 10, True),
+    ("hard_frm_512x512x64_bf16", 4, 20, False),
+]
+
+
+@pytest.mark.parametrize("name,S,it,batched", OUTPUT_PATH_CASES)
+def test_frm_output_paths_agree(ddm, name, S, it, batched):
+    """The one-workgroup bitmap output and the collection kernel + multi-workgroup compaction give
+    the same bits: pairs, scores, per-seed states, query counts (in the default mode)."""
+    import torch
+    pairs = synth.make_config(name)
+    D1 = torch.stack([dev(p.D1, p.dtype) for p in pairs]); D2 = torch.stack([dev(p.D2, p.dtype) for p in pairs])
+    if not batched:
+        D1, D2 = D1[0], D2[0]
+    p0 = pairs[0]
+    buf = ddm.FrmBuffers(len(pairs), p0.H1, p0.W1, p0.H2, p0.W2, p0.d, D1.dtype, S, it, D1.device)
+    runs = []
+    try:
+        for limit in (-1, 0, -1):
+            ddm.debug_set_output_bitmap_limit(limit)
+            buf.count.fill_(-3); buf.qcounts.fill_(-3); buf.state.fill_(-3)
+            buf.out_i.fill_(-5); buf.out_j.fill_(-5)
+            ddm.frm_match_into(D1, D2, S, it, buf, batched=batched)
+            torch.cuda.synchronize()
+            runs.append(_frm_outputs(buf))
+    finally:
+        ddm.debug_set_output_bitmap_limit(-1)
+    for r in runs[1:]:
+        _assert_same(r, runs[0], f"{name} output paths")
+
+
+def test_frm_output_paths_agree_with_routine_options(ddm):
+    """Explicit starts (with repeats and out-of-map entries), pixel_tol and the basin map through
+    both output paths."""
+    import torch
+    (p,) = synth.make_config("frm_512x384x24_f16")
+    D1, D2 = dev(p.D1, p.dtype), dev(p.D2, p.dtype)
+    rng = np.random.default_rng(9)
+    starts = torch.tensor(np.concatenate([rng.integers(0, p.H1 * p.W1, 3000), [5, 5, -1, p.H1 * p.W1]]),
+                          dtype=torch.int32, device="cuda")
+    runs = []
+    try:
+        for limit in (-1, 0):
+            ddm.debug_set_output_bitmap_limit(limit)
+            runs.append(ddm.frm_match_ex(D1, D2, starts=starts, max_iter=4, pixel_tol=1.5, ret_basin=True,
+                                         return_state=True))
+    finally:
+        ddm.debug_set_output_bitmap_limit(-1)
+    a, b = runs
+    assert a[0].numel() > 100
+    for x, y in zip(a[:4], b[:4]):
+        assert torch.equal(x, y)
+    assert torch.equal(a[-1]["state"], b[-1]["state"]) and torch.equal(a[-1]["query_counts"], b[-1]["query_counts"])
