@@ -596,9 +596,13 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
     uint32_t *ctl = (uint32_t *)(w + P.o_ctl);
     int32_t *marks = P.explicit_starts ? (int32_t *)(w + P.o_marks) : nullptr;
 
-    const int init_blocks = (int)std::min<long long>((std::max(P.k, P.N1) + 255) / 256, 4096);
-    hipLaunchKernelGGL(frm_init_kernel, dim3(init_blocks, P.B), dim3(256), 0, s, st, P.k, std::max(P.kx, 1),
-                       P.W1, P.S, P.N1, P.nhalf, ctl, marks);
+    // The one-workgroup output reads no dense match array, so unless start marks or a basin map
+    // need clearing, the image-1-sized arrays are left alone.
+    const bool bitmap_out = P.N1 <= output_bitmap_limit().load() && P.k <= OUT_NT * OUT_SPT;
+    const int n1_clear = (bitmap_out && !marks && !O.basin) ? 0 : P.N1;
+    const int init_blocks = (int)std::min<long long>((std::max(P.k, n1_clear) + 255) / 256, 4096);
+    hipLaunchKernelGGL(frm_init_kernel, dim3(std::max(init_blocks, 1), P.B), dim3(256), 0, s, st, P.k,
+                       std::max(P.kx, 1), P.W1, P.S, n1_clear, P.nhalf, ctl, marks);
     DDM_CHECK_LAUNCH();
     if (P.explicit_starts && P.k > 0) {
         // distinct starts, ascending: marks -> ordered compaction into u / qrows[0], count into counts[0]
@@ -636,7 +640,7 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
             DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, which, &fa, h_split, P.loop_lds, ntask, s, true); }));
         }
     }
-    if (P.N1 <= output_bitmap_limit().load() && P.k <= OUT_NT * OUT_SPT) {
+    if (bitmap_out) {
         // one workgroup per pair: collection and ordered output through an LDS bitmap
         hipLaunchKernelGGL(frm_output_kernel, dim3(P.B), dim3(OUT_NT), (size_t)(P.N1 + 31) / 32 * 8, s, st, P.k,
                            seed_state, (const int32_t *)st.counts, query_counts, P.nhalf, P.W1, O.pixel_tol,

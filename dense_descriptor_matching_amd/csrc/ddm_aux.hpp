@@ -283,9 +283,10 @@ __device__ __forceinline__ void frm_seed_reset(const FrmState &st, long long ka,
 // Initial state. Grid seeds (k > 0 of them: rows S/2 + S*n < H1, columns
 // S/2 + S*n < W1, p = x + W1*y, ascending) are written here; with explicit
 // starts (marks != null) the seeds come later from the start marks and the
-// kernel only clears the marks. Also clears the dense match array, the basin
-// map and the control words of the loop and tail kernels (barrier arrivals,
-// error flag, ticket, done and ready counters).
+// kernel only clears the marks. Also clears the first n1 entries of the dense
+// match array, the marks and the basin map (n1 = 0 when none of them is read:
+// the one-workgroup output), and the control words of the loop and tail
+// kernels (barrier arrivals, error flag, ticket, done and ready counters).
 __global__ void __launch_bounds__(256) frm_init_kernel(FrmState st, int k, int kx, int W1, int S, int N1,
                                                        int nhalf, uint32_t *ctl, int32_t *marks) {
     if (ctl && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 5) ctl[threadIdx.x * 32] = 0;
