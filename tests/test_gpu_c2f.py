@@ -91,3 +91,24 @@ def test_c2f_rejects_bad_sizes(ddm):
     y = torch.zeros(64, 48, 23, dtype=torch.float16, device="cuda")
     with pytest.raises(ddm.DDMError):
         ddm.c2f_match(y, y, crop=(32, 24))
+
+
+@pytest.mark.parametrize("case", [0, 2, 4])
+def test_c2f_output_paths_agree(ddm, case):
+    """The coarse and the fine FRM inside coarse-to-fine through the one-workgroup bitmap output
+    and through the multi-workgroup compaction: identical pairs, scores and crop windows."""
+    H, W, d, dt, seed, shift, sigma, factor, cs, crop, fs = CASES[case]
+    p = synth.make_pair(H, W, d, dt, seed, sigma=sigma, shift=shift)
+    F1, F2 = dev(p.D1, p.dtype), dev(p.D2, p.dtype)
+    runs = []
+    try:
+        for limit in (-1, 0):
+            ddm.debug_set_output_bitmap_limit(limit)
+            runs.append([t.cpu().numpy() for t in ddm.c2f_match(F1, F2, factor=factor, coarse_stride=cs,
+                                                                coarse_iter=10, crop=crop, fine_stride=fs,
+                                                                fine_iter=10, return_crops=True)])
+    finally:
+        ddm.debug_set_output_bitmap_limit(-1)
+    assert runs[0][0].size > 100
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
