@@ -119,11 +119,12 @@ __device__ __forceinline__ void rescan_one(uint64_t k, const unsigned char *qp, 
 // NT / 16 queries per round. emit(valid, x, j, s, sub) is called by every lane
 // in every round (wave-wide ballots may follow). A block past nq returns at
 // once (nq may come from device memory; the test is uniform over the block).
-// The caller separates two uses of red by a barrier.
-template <int DT, int QB, int NT, class QPtr, class Emit>
+// The caller separates two uses of red by a barrier. mid() runs on every
+// thread between the phases (loads issued there travel with the candidates').
+template <int DT, int QB, int NT, class QPtr, class Emit, class Mid>
 __device__ __forceinline__ void resolve_block(int blk, uint64_t *red, const uint64_t *part, int nchunks,
                                               long long rowcap, int nq, const unsigned char *R, int nref, int ld,
-                                              int d, QPtr qptr, Emit emit) {
+                                              int d, QPtr qptr, Emit emit, Mid mid) {
     static_assert(QB % 16 == 0 && NT % QB == 0 && QB % (NT / 16) == 0, "QB and NT");
     constexpr int TPQ = NT / QB, PER_ROUND = NT / 16;
     const int x0 = blk * QB;
@@ -152,6 +153,7 @@ __device__ __forceinline__ void resolve_block(int blk, uint64_t *red, const uint
         red[threadIdx.x] = k;
     }
     if (TPQ > 1) __syncthreads();
+    mid();
     const int sub = threadIdx.x & 15;
 #pragma unroll 1
     for (int round = 0; round < QB / PER_ROUND; ++round) {
@@ -163,6 +165,13 @@ __device__ __forceinline__ void resolve_block(int blk, uint64_t *red, const uint
         if (valid) rescan_one<DT>(red[r], qptr(x), R, nref, ld, d, sub, &j, &s);
         emit(valid, x, j, s, sub);
     }
+}
+
+template <int DT, int QB, int NT, class QPtr, class Emit>
+__device__ __forceinline__ void resolve_block(int blk, uint64_t *red, const uint64_t *part, int nchunks,
+                                              long long rowcap, int nq, const unsigned char *R, int nref, int ld,
+                                              int d, QPtr qptr, Emit emit) {
+    resolve_block<DT, QB, NT>(blk, red, part, nchunks, rowcap, nq, R, nref, ld, d, qptr, emit, [] {});
 }
 
 struct ResolveArgs {
@@ -341,22 +350,33 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
     if (x0 >= nq) return;
     const unsigned char *Q = a.Q + pair * a.q_bs;
     const SplitGeom sg = split_geom(a.split, nq, a.split_rows, a.qblocks, a.chunk_groups, a.nchunks, a.rowcap);
+    // The query of this thread's rescan (one round: QB = NT / 16): its row index and
+    // seed are loaded before the partial merge, the seed's previous pixel between
+    // merge and rescan, so that they arrive with the partials and the candidates.
+    static_assert(QB == NT / 16, "one rescan round per block");
+    const int xm = x0 + (int)(threadIdx.x >> 4);
+    const bool vm = xm < nq;
+    int pre_qrow = 0, pre_seed = 0, pre_prev = 0;
+    if (vm) {
+        pre_qrow = st.qrows[cur][ko + xm];
+        pre_seed = st.act[cur][ko + xm];
+    }
     resolve_block<DT, QB, NT>(
         blk, red, a.rowpart + pair * a.rowpart_bs, a.nchunks * sg.s, sg.rowcap, nq, a.R + pair * a.r_bs, a.nref,
         a.ld, a.d,
-        [&](int x) { return Q + (long long)st.qrows[cur][ko + x] * a.ld * Tr<DT>::ESZ; },
+        [&](int) { return Q + (long long)pre_qrow * a.ld * Tr<DT>::ESZ; },
         [&](bool valid, int x, int j, float s, int sub) {
             if (sub != 0) return;
             int seed = -1;
             if (valid) {
-                seed = st.act[cur][ko + x];
+                seed = pre_seed;
                 bool keep;
                 if (!backward) {
-                    keep = st.basin != nullptr || j != st.v[ko + seed];    // no forward test in the basin variant
+                    keep = st.basin != nullptr || j != pre_prev;    // no forward test in the basin variant
                     st.v[ko + seed] = j;
                     st.score[ko + seed] = reported(s, a.neg_out);
                 } else {
-                    const int from = st.u[ko + seed];
+                    const int from = pre_prev;
                     keep = (j != from);
                     st.u[ko + seed] = j;
                     st.uprev[ko + seed] = from;
@@ -370,6 +390,9 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
             }
             keep_seed[x - x0] = seed;
             keep_j[x - x0] = j;
+        },
+        [&] {
+            if (vm) pre_prev = backward ? st.u[ko + pre_seed] : st.v[ko + pre_seed];
         });
     __syncthreads();
     if (threadIdx.x < 64) {
