@@ -102,3 +102,41 @@ def test_inside_caller_graph_capture(ddm, maps):
         _same(_frm_out(fb), ref_f)
         _same(_mut_out(mb), ref_m)
         del x
+
+
+def test_concurrent_calls_on_two_streams(ddm):
+    """Two FRM calls (each with its own buffers) and a mutual call enqueued on two streams at once,
+    several times over: the ticket-ordered tail kernels of concurrent calls compete for the CUs and
+    must still finish with the results of lone calls (their waits only depend on workgroups of
+    their own launch that already run)."""
+    import torch
+    p = synth.make_pair(512, 384, 24, synth.F16, 83, sigma=0.15, shift=(9, -4))
+    q = synth.make_pair(256, 192, 24, synth.F16, 84, sigma=0.2, shift=(-5, 6))
+    from synth.torchio import to_device
+    A1, A2 = to_device(p.D1, p.dtype, "cuda"), to_device(p.D2, p.dtype, "cuda")
+    B1, B2 = to_device(q.D1, q.dtype, "cuda"), to_device(q.D2, q.dtype, "cuda")
+    fa = ddm.FrmBuffers(1, 512, 384, 512, 384, 24, torch.float16, 8, 10, A1.device)
+    fb = ddm.FrmBuffers(1, 256, 192, 256, 192, 24, torch.float16, 4, 10, B1.device)
+    mb = ddm.MutualBuffers(256, 192, 256, 192, 24, torch.float16, B1.device)
+    ddm.frm_match_into(A1, A2, 8, 10, fa)
+    ddm.frm_match_into(B1, B2, 4, 10, fb)
+    ddm.mutual_nn_into(B1, B2, mb)
+    torch.cuda.synchronize()
+    ref_a, ref_b, ref_m = _frm_out(fa), _frm_out(fb), _mut_out(mb)
+    assert ref_a[0].numel() > 1000 and ref_b[0].numel() > 1000
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(5):
+        _scribble(fa, mb)
+        _scribble(fb, mb)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            ddm.frm_match_into(A1, A2, 8, 10, fa)
+        with torch.cuda.stream(s2):
+            ddm.frm_match_into(B1, B2, 4, 10, fb)
+            ddm.mutual_nn_into(B1, B2, mb)
+        with torch.cuda.stream(s1):
+            ddm.frm_match_into(A1, A2, 8, 10, fa)       # a second call on s1 overlapping s2's mutual
+        torch.cuda.synchronize()
+        _same(_frm_out(fa), ref_a)
+        _same(_frm_out(fb), ref_b)
+        _same(_mut_out(mb), ref_m)
