@@ -356,3 +356,39 @@ def test_frm_output_paths_agree_with_routine_options(ddm):
     for x, y in zip(a[:4], b[:4]):
         assert torch.equal(x, y)
     assert torch.equal(a[-1]["state"], b[-1]["state"]) and torch.equal(a[-1]["query_counts"], b[-1]["query_counts"])
+
+
+OUTPUT_LIMIT_CASES = [
+    # (H1, W1, stride or None, explicit starts) around the one-workgroup output's limits
+    (1024, 512, 16, None),          # 2^19 image-1 pixels: the largest bitmap (128 KB of LDS), 2048 seeds
+    (1025, 512, 16, None),          # one row more: the multi-workgroup path
+    (512, 512, 8, None),            # exactly 4096 grid seeds
+    (384, 256, None, 4096),         # 4096 explicit starts (with repeats)
+    (384, 256, None, 4097),         # 4097: the multi-workgroup path
+]
+
+
+@pytest.mark.parametrize("H,W,S,nstarts", OUTPUT_LIMIT_CASES)
+def test_frm_output_paths_at_their_limits(ddm, H, W, S, nstarts):
+    """Both output paths, bit for bit, at and just past the pixel and seed limits of the
+    one-workgroup bitmap output."""
+    import torch
+    p = synth.make_pair(H, W, 24, synth.F16, 97, sigma=0.1, shift=(6, -5))
+    D1, D2 = dev(p.D1, p.dtype), dev(p.D2, p.dtype)
+    runs = []
+    try:
+        for limit in (-1, 0):
+            ddm.debug_set_output_bitmap_limit(limit)
+            if nstarts is None:
+                runs.append(ddm.frm_match(D1, D2, S, 10, return_state=True))
+            else:
+                starts = torch.tensor(np.random.default_rng(nstarts).integers(0, H * W, nstarts), dtype=torch.int32,
+                                      device="cuda")
+                runs.append(ddm.frm_match_ex(D1, D2, starts=starts, max_iter=5, pixel_tol=1.5, return_state=True))
+    finally:
+        ddm.debug_set_output_bitmap_limit(-1)
+    a, b = runs
+    assert a[0].numel() > 500
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    assert torch.equal(a[-1]["state"], b[-1]["state"]) and torch.equal(a[-1]["query_counts"], b[-1]["query_counts"])
