@@ -175,8 +175,8 @@ int ddm_frm_match_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
  *   DDM_FRM_LOOP: every iteration in one cooperative kernel that loops over
  *     the half-steps with grid barriers and stops as soon as no seed is active
  *     (the device must support cooperative launches, else per half-step).
- *     Its barriers cost more than kernel boundaries on large maps; it pays off
- *     on small ones.
+ *     Its barriers cost more than kernel boundaries on large maps; on small
+ *     ones it beats per-half-step launches but not DDM_FRM_TAIL.
  *   DDM_FRM_TAIL (default): the first iterations per half-step (see
  *     ddm_frm_set_tail_after), the rest in one plain kernel launch whose
  *     workgroups take the remaining tasks in a global order from a ticket
