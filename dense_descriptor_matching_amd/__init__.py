@@ -152,7 +152,7 @@ def frm_get_mode() -> int:
 
 def frm_set_tail_after(iterations: int):
     """Iterations run per half-step before the tail kernel takes over in FRM_TAIL mode
-    (-1, the default: one for small problems, three for large ones)."""
+    (-1, the default: 2 to 8 half-steps, later for larger problems)."""
     _rc(lib().ddm_frm_set_tail_after(iterations), "ddm_frm_set_tail_after")
 
 

@@ -547,17 +547,21 @@ std::atomic<int> &tail_after() { static std::atomic<int> n{-1}; return n; }
 
 // Launch plan of a call in the effective mode `mode` (the caller has already
 // replaced the loop mode where the device has no cooperative launches).
-// Automatic split: kernel boundaries cost less than the tail kernel's
-// completion counters and waits while a half-step has much work, so large
-// problems run the first three iterations (which hold nearly all the work on
-// shifted or moderately distorted pairs) per half-step; small ones hand over
-// after one, where launch overheads dominate.
+// Automatic split, in half-steps: kernel boundaries cost less than the tail
+// kernel's completion counters and waits while a half-step has much work, and
+// larger problems keep real work in later half-steps (more seeds, larger maps,
+// slower convergence), so the hand-over moves later with w = pairs x seeds x
+// image-2 pixels: after 2 half-steps up to 2^24, 3 up to 2^27, 5 up to 2^31,
+// else 8 (the best of 2..8 on each of six measured workloads, 64x48 to
+// 16 x 512x384 and 512x512x64).
 FrmExec frm_exec(int mode, const FrmPlan &P) {
     if (mode == DDM_FRM_LOOP) return {0, 1};
     if (mode == DDM_FRM_TAIL) {
-        int it = tail_after().load();
-        if (it < 0) it = (long long)P.B * P.k * P.N2 <= (1LL << 27) ? 1 : 3;
-        return {std::min(P.nhalf, 2 * it), 2};
+        const int it = tail_after().load();
+        if (it >= 0) return {std::min(P.nhalf, 2 * it), 2};
+        const long long w = (long long)P.B * P.k * P.N2;
+        const int hs = w <= (1LL << 24) ? 2 : w <= (1LL << 27) ? 3 : w <= (1LL << 31) ? 5 : 8;
+        return {std::min(P.nhalf, hs), 2};
     }
     return {P.nhalf, 0};
 }

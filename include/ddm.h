@@ -192,8 +192,9 @@ typedef enum { DDM_FRM_PER_HALF_STEP = 0, DDM_FRM_LOOP = 1, DDM_FRM_TAIL = 2 } d
 int ddm_frm_set_mode(int mode);
 int ddm_frm_get_mode(void);
 /* Iterations run per half-step before the tail kernel takes over in DDM_FRM_TAIL (0..DDM_MAX_ITER;
- * 0 runs every half-step in the tail kernel). -1 (the default) chooses by size: one iteration when
- * pairs x seeds x image-2 pixels <= 2^27, else three. Process-wide; DDM_ERR_INVALID outside
+ * 0 runs every half-step in the tail kernel). -1 (the default) chooses by size, in half-steps:
+ * with w = pairs x seeds x image-2 pixels, the tail kernel starts after 2 half-steps when
+ * w <= 2^24, 3 when w <= 2^27, 5 when w <= 2^31, else 8. Process-wide; DDM_ERR_INVALID outside
  * -1..DDM_MAX_ITER. */
 int ddm_frm_set_tail_after(int iterations);
 /* Test aid for the failure path of DDM_FRM_LOOP and DDM_FRM_TAIL: the number of polls a wait makes
