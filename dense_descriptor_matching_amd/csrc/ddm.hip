@@ -604,10 +604,17 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
     // need clearing, the image-1-sized arrays are left alone.
     const bool bitmap_out = P.N1 <= output_bitmap_limit().load() && P.k <= OUT_NT * OUT_SPT;
     const int n1_clear = (bitmap_out && !marks && !O.basin) ? 0 : P.N1;
-    const int init_blocks = (int)std::min<long long>((std::max(P.k, n1_clear) + 255) / 256, 4096);
-    hipLaunchKernelGGL(frm_init_kernel, dim3(std::max(init_blocks, 1), P.B), dim3(256), 0, s, st, P.k,
-                       std::max(P.kx, 1), P.W1, P.S, n1_clear, P.nhalf, ctl, marks);
-    DDM_CHECK_LAUNCH();
+    // Grid seeds with nothing image-1-sized to clear and a first half-step launched on its own
+    // need no init kernel: that sweep derives their pixels and resets the counts and control
+    // words, its update writes their initial state.
+    const int h_split = std::max(0, std::min(E.h_split, P.nhalf));
+    const bool implicit_seeds = !P.explicit_starts && n1_clear == 0 && h_split >= 1 && P.k > 0;
+    if (!implicit_seeds) {
+        const int init_blocks = (int)std::min<long long>((std::max(P.k, n1_clear) + 255) / 256, 4096);
+        hipLaunchKernelGGL(frm_init_kernel, dim3(std::max(init_blocks, 1), P.B), dim3(256), 0, s, st, P.k,
+                           std::max(P.kx, 1), P.W1, P.S, n1_clear, P.nhalf, ctl, marks);
+        DDM_CHECK_LAUNCH();
+    }
     if (P.explicit_starts && P.k > 0) {
         // distinct starts, ascending: marks -> ordered compaction into u / qrows[0], count into counts[0]
         const int mb = (int)std::min<long long>((P.k + 255) / 256, 4096);
@@ -628,9 +635,9 @@ int frm_run(const FrmPlan &P, const FrmOpts &O, const void *D1, const void *D2, 
         fa.nch[0] = P.nch2; fa.nch[1] = P.nch1;
         fa.bar = ctl; fa.err = (int32_t *)(ctl + 32); fa.spin_limit = loop_spin_limit().load();
         fa.tail = ctl + 64;
+        if (implicit_seeds) fa.g0 = GridSeeds{P.S, std::max(P.kx, 1), P.W1, P.k};
         const long long sweep_tasks = (long long)P.B * P.qblocks * std::max(P.nch1, P.nch2);
         const long long upd_tasks = (long long)P.B * ((P.k + 15) / 16);
-        const int h_split = std::max(0, std::min(E.h_split, P.nhalf));
         for (int h = 0; h < h_split; ++h) {
             DDM_CHECK(with_events(2, s, [&] { return frm_switch(f, 0, &fa, h, P.loop_lds, sweep_tasks, s, true); }));
             DDM_DT_SWITCH(f.dtype, frm_update_kernel, dim3((unsigned)capped_grid(std::min<long long>(upd_tasks, 2048))),

@@ -283,6 +283,12 @@ struct FrmState {
     long long n1_bs;       // elements between pairs for match arrays
 };
 
+// Grid seeds left implicit in the first half-step (S = 0: none): the first
+// sweep derives their pixels, the first update writes their initial state.
+struct GridSeeds {
+    int S, kx, W, k;
+};
+
 __device__ __forceinline__ void frm_seed_reset(const FrmState &st, long long ka, int a, int p) {
     st.u[ka] = p; st.v[ka] = -1; st.conv[ka] = -1; st.score[ka] = 0.f;
     st.act[0][ka] = a; st.qrows[0][ka] = p;
@@ -339,13 +345,14 @@ __global__ void __launch_bounds__(256) frm_seeds_from_starts_kernel(FrmState st,
 // address); list order does not affect any result.
 template <int DT, int QB, int NT>
 __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmState &st, int h, int backward,
-                                                int iter, int pair, int blk, uint64_t *red) {
+                                                int iter, int pair, int blk, uint64_t *red, GridSeeds g0) {
     static_assert(QB <= 64, "survivors of a block are gathered by one wave");
     __shared__ int keep_seed[QB], keep_j[QB];
     const int cur = h & 1, nxt = cur ^ 1;
     const long long ko = pair * st.k_bs;
     int32_t *counts = st.counts + pair * st.cnt_bs;
-    const int nq = counts[h];
+    const bool implicit = h == 0 && g0.S > 0;       // seed x at its grid pixel, no state yet
+    const int nq = implicit ? g0.k : counts[h];
     const int x0 = blk * QB;
     if (x0 >= nq) return;
     const unsigned char *Q = a.Q + pair * a.q_bs;
@@ -358,8 +365,8 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
     const bool vm = xm < nq;
     int pre_qrow = 0, pre_seed = 0, pre_prev = 0;
     if (vm) {
-        pre_qrow = st.qrows[cur][ko + xm];
-        pre_seed = st.act[cur][ko + xm];
+        pre_qrow = implicit ? grid_seed_pixel(xm, g0.S, g0.kx, g0.W) : st.qrows[cur][ko + xm];
+        pre_seed = implicit ? xm : st.act[cur][ko + xm];
     }
     resolve_block<DT, QB, NT>(
         blk, red, a.rowpart + pair * a.rowpart_bs, a.nchunks * sg.s, sg.rowcap, nq, a.R + pair * a.r_bs, a.nref,
@@ -375,6 +382,10 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
                     keep = st.basin != nullptr || j != pre_prev;    // no forward test in the basin variant
                     st.v[ko + seed] = j;
                     st.score[ko + seed] = reported(s, a.neg_out);
+                    if (implicit) {                                 // the seed's initial state
+                        st.u[ko + seed] = pre_qrow; st.uprev[ko + seed] = pre_qrow;
+                        st.uiter[ko + seed] = -1; st.conv[ko + seed] = -1;
+                    }
                 } else {
                     const int from = pre_prev;
                     keep = (j != from);
@@ -392,7 +403,7 @@ __device__ __forceinline__ void frm_update_task(const ResolveArgs &a, const FrmS
             keep_j[x - x0] = j;
         },
         [&] {
-            if (vm) pre_prev = backward ? st.u[ko + pre_seed] : st.v[ko + pre_seed];
+            if (vm) pre_prev = implicit ? -1 : backward ? st.u[ko + pre_seed] : st.v[ko + pre_seed];
         });
     __syncthreads();
     if (threadIdx.x < 64) {

@@ -35,7 +35,25 @@ struct FrmArgs {
     int32_t *err;         // loop and tail kernels: set to 1 when a wait ran past its bound
     int spin_limit;       // loop and tail kernels: polls per wait before giving up
     uint32_t *tail;       // tail kernel: ticket, done and ready words at +0, +32, +64, zero at launch
+    GridSeeds g0;         // grid seeds implicit in half-step 0 (g0.S = 0: the init kernel wrote them)
 };
+
+// Active queries of pair pr at half-step h. Every helper below takes the grid
+// seeds of half-step 0 separately: the per-half-step kernels pass a.g0, the
+// loop and tail kernels (which never start at an implicit half-step 0) pass a
+// zero constant, so that path is compiled out of them.
+__device__ __forceinline__ int frm_count(const FrmArgs &a, GridSeeds g0, int h, int pr) {
+    return (h == 0 && g0.S > 0) ? g0.k : a.st.counts[pr * a.st.cnt_bs + h];
+}
+
+// Start of a call whose grid seeds are implicit in half-step 0 (one workgroup
+// of the first sweep): the active counts (k, then zero) and the control words.
+__device__ __forceinline__ void frm_grid_start(const FrmArgs &a) {
+    if (threadIdx.x < 5) a.bar[threadIdx.x * 32] = 0;
+    const int per = a.nhalf + 1;
+    for (int i = threadIdx.x; i < a.B * per; i += blockDim.x)
+        a.st.counts[(i / per) * a.st.cnt_bs + i % per] = (i % per == 0) ? a.k : 0;
+}
 
 // Task t of a phase -> (pair, task within the pair), given the per-pair counts.
 template <class Count>
@@ -51,19 +69,28 @@ __device__ __forceinline__ int task_locate(int B, int t, Count count, int *pair)
 }
 
 // Sweep arguments of half-step h: its direction, query list and counts.
-__device__ __forceinline__ SweepArgs frm_sweep_args(const FrmArgs &a, int h) {
+__device__ __forceinline__ SweepArgs frm_sweep_args(const FrmArgs &a, GridSeeds g0, int h) {
     SweepArgs p = a.sw[h & 1];
+    if (h == 0 && g0.S > 0) {             // implicit grid seeds: rows from the grid, k of them
+        p.qrows = nullptr;
+        p.qcount = nullptr;
+        p.nq = g0.k;
+        p.grid_s = g0.S; p.grid_kx = g0.kx; p.grid_w = g0.W;
+        return p;
+    }
     p.qrows = a.st.qrows[h & 1];
     p.qcount = a.st.counts + h;
+    p.grid_s = 0;
     return p;
 }
 
 // Sweep tasks of pair pr at half-step h: reference chunks x query groups of
 // the runtime split (0 when the pair has no active query).
 template <int DT>
-__device__ __forceinline__ int frm_sweep_tasks(const FrmArgs &a, const SweepArgs &p, int h, int pr) {
+__device__ __forceinline__ int frm_sweep_tasks(const FrmArgs &a, GridSeeds g0, const SweepArgs &p, int h,
+                                           int pr) {
     constexpr int GROUP = TILE * group_tiles(DT);
-    const int nq = a.st.counts[pr * a.st.cnt_bs + h];
+    const int nq = frm_count(a, g0, h, pr);
     if (nq <= 0) return 0;
     const int nch = a.nch[h & 1];
     const SplitGeom sg = split_geom(p.split, nq, p.split_rows, p.qblocks, p.chunk / GROUP, nch, p.rowcap);
@@ -71,75 +98,76 @@ __device__ __forceinline__ int frm_sweep_tasks(const FrmArgs &a, const SweepArgs
 }
 
 template <int DT>
-__device__ __forceinline__ int frm_sweep_total(const FrmArgs &a, const SweepArgs &p, int h) {
+__device__ __forceinline__ int frm_sweep_total(const FrmArgs &a, GridSeeds g0, const SweepArgs &p, int h) {
     int total = 0;
-    for (int pr = 0; pr < a.B; ++pr) total += frm_sweep_tasks<DT>(a, p, h, pr);
+    for (int pr = 0; pr < a.B; ++pr) total += frm_sweep_tasks<DT>(a, g0, p, h, pr);
     return total;
 }
 
 // Sweep task t (over all pairs) of half-step h.
 template <int DT, int NP, int NKB, int RQ, int NW>
-__device__ __forceinline__ void frm_sweep_run(const FrmArgs &a, const SweepArgs &p, int h, int t,
-                                              unsigned char *lds) {
+__device__ __forceinline__ void frm_sweep_run(const FrmArgs &a, GridSeeds g0, const SweepArgs &p, int h,
+                                              int t, unsigned char *lds) {
     int pr;
-    const int tt = task_locate(a.B, t, [&](int q) { return frm_sweep_tasks<DT>(a, p, h, q); }, &pr);
+    const int tt = task_locate(a.B, t, [&](int q) { return frm_sweep_tasks<DT>(a, g0, p, h, q); }, &pr);
     const int nch = a.nch[h & 1];
     sweep_task<DT, NP, NKB, RQ, NW, false>(p, pr, tt % nch, tt / nch, lds);
 }
 
 // Sweep phase of half-step h over the workgroups of the grid.
 template <int DT, int NP, int NKB, int RQ, int NW>
-__device__ __forceinline__ void frm_sweep_phase(const FrmArgs &a, int h, unsigned char *lds) {
-    const SweepArgs p = frm_sweep_args(a, h);
-    const int total = frm_sweep_total<DT>(a, p, h);
+__device__ __forceinline__ void frm_sweep_phase(const FrmArgs &a, GridSeeds g0, int h, unsigned char *lds) {
+    const SweepArgs p = frm_sweep_args(a, g0, h);
+    const int total = frm_sweep_total<DT>(a, g0, p, h);
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         __syncthreads();                       // the previous task's waves are done with the LDS
-        frm_sweep_run<DT, NP, NKB, RQ, NW>(a, p, h, t, lds);
+        frm_sweep_run<DT, NP, NKB, RQ, NW>(a, g0, p, h, t, lds);
     }
 }
 
 // Update tasks of pair pr at half-step h: blocks of QB active queries.
 template <int QB>
-__device__ __forceinline__ int frm_update_tasks(const FrmArgs &a, int h, int pr) {
-    return (a.st.counts[pr * a.st.cnt_bs + h] + QB - 1) / QB;
+__device__ __forceinline__ int frm_update_tasks(const FrmArgs &a, GridSeeds g0, int h, int pr) {
+    return (frm_count(a, g0, h, pr) + QB - 1) / QB;
 }
 
 template <int QB>
-__device__ __forceinline__ int frm_update_total(const FrmArgs &a, int h) {
+__device__ __forceinline__ int frm_update_total(const FrmArgs &a, GridSeeds g0, int h) {
     int total = 0;
-    for (int pr = 0; pr < a.B; ++pr) total += frm_update_tasks<QB>(a, h, pr);
+    for (int pr = 0; pr < a.B; ++pr) total += frm_update_tasks<QB>(a, g0, h, pr);
     return total;
 }
 
 // Update task t (over all pairs) of half-step h with NT threads, NT/16 queries.
 template <int DT, int NT>
-__device__ __forceinline__ void frm_update_run(const FrmArgs &a, int h, int t, uint64_t *red) {
+__device__ __forceinline__ void frm_update_run(const FrmArgs &a, GridSeeds g0, int h, int t, uint64_t *red) {
     constexpr int QB = NT / 16;
     int pr;
-    const int blk = task_locate(a.B, t, [&](int q) { return frm_update_tasks<QB>(a, h, q); }, &pr);
-    frm_update_task<DT, QB, NT>(a.rs[h & 1], a.st, h, h & 1, h / 2 + 1, pr, blk, red);
+    const int blk = task_locate(a.B, t, [&](int q) { return frm_update_tasks<QB>(a, g0, h, q); }, &pr);
+    frm_update_task<DT, QB, NT>(a.rs[h & 1], a.st, h, h & 1, h / 2 + 1, pr, blk, red, g0);
 }
 
 // Update phase of half-step h over the workgroups of the grid.
 template <int DT, int NT>
-__device__ __forceinline__ void frm_update_phase(const FrmArgs &a, int h, uint64_t *red) {
-    const int total = frm_update_total<NT / 16>(a, h);
+__device__ __forceinline__ void frm_update_phase(const FrmArgs &a, GridSeeds g0, int h, uint64_t *red) {
+    const int total = frm_update_total<NT / 16>(a, g0, h);
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         __syncthreads();
-        frm_update_run<DT, NT>(a, h, t, red);
+        frm_update_run<DT, NT>(a, g0, h, t, red);
     }
 }
 
 template <int DT, int NP, int NKB, int RQ, int NW>
 __global__ void __launch_bounds__(NW * 64) frm_sweep_kernel(FrmArgs a, int h) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    frm_sweep_phase<DT, NP, NKB, RQ, NW>(a, h, lds);
+    if (h == 0 && a.g0.S > 0 && blockIdx.x == 0) frm_grid_start(a);
+    frm_sweep_phase<DT, NP, NKB, RQ, NW>(a, a.g0, h, lds);
 }
 
 template <int DT>
 __global__ void __launch_bounds__(256) frm_update_kernel(FrmArgs a, int h) {
     __shared__ uint64_t red[256];
-    frm_update_phase<DT, 256>(a, h, red);
+    frm_update_phase<DT, 256>(a, a.g0, h, red);
 }
 
 constexpr int kSpinLimit = 1 << 20;   // default polls per barrier wait (each an uncached load + s_sleep): ~1 s
@@ -175,15 +203,16 @@ template <int DT, int NP, int NKB, int RQ, int NW>
 __global__ void __launch_bounds__(NW * 64) frm_loop_kernel(FrmArgs a, int h_begin) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int flag;
+    constexpr GridSeeds none{};
     uint32_t target = 0;
     for (int h = h_begin; h < a.nhalf; ++h) {
         bool any = false;
-        for (int pr = 0; pr < a.B; ++pr) any |= a.st.counts[pr * a.st.cnt_bs + h] > 0;
+        for (int pr = 0; pr < a.B; ++pr) any |= frm_count(a, none, h, pr) > 0;
         if (!any) break;
-        frm_sweep_phase<DT, NP, NKB, RQ, NW>(a, h, lds);
+        frm_sweep_phase<DT, NP, NKB, RQ, NW>(a, none, h, lds);
         target += gridDim.x;
         if (!grid_sync(a.bar, target, a.err, a.spin_limit, &flag)) return;
-        frm_update_phase<DT, NW * 64>(a, h, reinterpret_cast<uint64_t *>(lds));
+        frm_update_phase<DT, NW * 64>(a, none, h, reinterpret_cast<uint64_t *>(lds));
         target += gridDim.x;
         if (!grid_sync(a.bar, target, a.err, a.spin_limit, &flag)) return;
     }
@@ -233,12 +262,13 @@ __global__ void __launch_bounds__(NW * 64) frm_tail_kernel(FrmArgs a, int h_begi
     __shared__ int flag;
     __shared__ uint32_t tk;
     constexpr int QB = NW * 64 / 16;
+    constexpr GridSeeds none{};
     uint32_t *ticket = a.tail, *done = a.tail + 32, *ready = a.tail + 64;
     int h = h_begin;
     if (h >= a.nhalf) return;
-    SweepArgs p = frm_sweep_args(a, h);
+    SweepArgs p = frm_sweep_args(a, none, h);
     uint32_t sb = 0;                                           // first ticket of half-step h
-    uint32_t ns = frm_sweep_total<DT>(a, p, h), nu = frm_update_total<QB>(a, h);
+    uint32_t ns = frm_sweep_total<DT>(a, none, p, h), nu = frm_update_total<QB>(a, none, h);
     if (ns == 0) return;
     for (;;) {
         __syncthreads();                                       // the LDS and tk are free again
@@ -249,17 +279,17 @@ __global__ void __launch_bounds__(NW * 64) frm_tail_kernel(FrmArgs a, int h_begi
             if (!tail_wait(ready, (uint32_t)(h + 1 - h_begin), a.err, a.spin_limit, &flag)) return;
             sb += ns + nu;
             if (++h >= a.nhalf) return;
-            p = frm_sweep_args(a, h);
-            ns = frm_sweep_total<DT>(a, p, h);
+            p = frm_sweep_args(a, none, h);
+            ns = frm_sweep_total<DT>(a, none, p, h);
             if (ns == 0) return;
-            nu = frm_update_total<QB>(a, h);
+            nu = frm_update_total<QB>(a, none, h);
         }
         const bool upd = t >= sb + ns;
         if (upd) {
             if (!tail_wait(done, sb + ns, a.err, a.spin_limit, &flag)) return;
-            frm_update_run<DT, NW * 64>(a, h, (int)(t - sb - ns), reinterpret_cast<uint64_t *>(lds));
+            frm_update_run<DT, NW * 64>(a, none, h, (int)(t - sb - ns), reinterpret_cast<uint64_t *>(lds));
         } else {
-            frm_sweep_run<DT, NP, NKB, RQ, NW>(a, p, h, (int)(t - sb), lds);
+            frm_sweep_run<DT, NP, NKB, RQ, NW>(a, none, p, h, (int)(t - sb), lds);
         }
         __syncthreads();                                       // every wave's writes of the task are issued
         if (threadIdx.x == 0) {

@@ -137,7 +137,16 @@ struct SweepArgs {
     int split;                   // tasks per pair to aim for; 0 = off
     int qblocks;                 // query blocks in the grid
     int split_rows;              // query rows per query block
+    // Implicit query rows (qrows null) of a one-way sweep: query x is the x-th seed
+    // of the stride-grid_s grid over a map of width grid_w with grid_kx seeds per
+    // row; 0 = rows 0, 1, ... (always so in the two-way sweep)
+    int grid_s, grid_kx, grid_w;
 };
+
+// Pixel of grid seed a: rows and columns S/2 + S*n, p = x + W*y, ascending.
+__device__ __forceinline__ int grid_seed_pixel(int a, int S, int kx, int W) {
+    return S / 2 + (a % kx) * S + W * (S / 2 + (a / kx) * S);
+}
 
 // Geometry of the runtime split for nq queries: query tasks per chunk (need),
 // sub-chunks per chunk (s), rows per partial slot (rowcap) and sub-blocks per
@@ -211,7 +220,8 @@ __device__ __forceinline__ void sweep_rows(const SweepArgs &p, const unsigned ch
 #pragma unroll
     for (int qt = 0; qt < RQ; ++qt) {
         int rr = min(row_of(qt) + c, nq - 1);
-        const int qrow = qrows ? qrows[rr] : rr;
+        const int qrow = qrows ? qrows[rr]
+                              : (!COLMAX && p.grid_s > 0) ? grid_seed_pixel(rr, p.grid_s, p.grid_kx, p.grid_w) : rr;
         const unsigned char *qp = Q + (long long)qrow * p.ld * ESZ;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
