@@ -6,7 +6,7 @@ seeds' initial state; every other execution (loop mode, the tail kernel from
 half-step 0, the multi-workgroup output path) starts with the init kernel.
 Cases: image 2 narrower and shorter than image 1 (the grid follows image 1's
 width), seed counts that are not a multiple of the 16-query update block,
-max_iter 1 and 4, one pair and three batched pairs. All four per-seed state
+max_iter 1 and 4, one to three batched pairs, fp16, bf16 and fp32 maps. All four per-seed state
 columns (u, v, conv_iter, u_old), pairs, scores and query counts must agree,
 and the implicit start must match the oracle.
 """
@@ -33,11 +33,11 @@ STARTS = (("per-half-step", 0, -1, None), ("tail default", 2, -1, None), ("tail 
           ("loop", 1, -1, None), ("tail from 0", 2, 0, None), ("dense output", 2, -1, 0))
 
 
-def _maps(B, seed):
+def _maps(B, seed, dtype):
     """B pairs of a 100 x 90 image 1 and a 96 x 70 image 2 cut from a noisy shifted copy."""
     D1, D2 = [], []
     for b in range(B):
-        p = synth.make_pair(100, 90, 24, synth.F16, seed + b, sigma=0.15, shift=(3, -2))
+        p = synth.make_pair(100, 90, 24, dtype, seed + b, sigma=0.15, shift=(3, -2))
         D1.append(p.D1)
         D2.append(np.ascontiguousarray(p.D2[2:98, 5:75]))
     return D1, D2, p.dtype
@@ -53,11 +53,14 @@ def _outputs(buf, B, k):
     return n, outs, buf.state.cpu().numpy().reshape(B, -1, 4)[:, :k].copy(), buf.qcounts.cpu().numpy().copy()
 
 
-@pytest.mark.parametrize("B,S,it", [(1, 7, 1), (1, 7, 4), (3, 7, 4), (3, 11, 1)])
-def test_frm_implicit_start_equals_init_start(ddm, B, S, it):
+@pytest.mark.parametrize("B,S,it,dtype", [(1, 7, 1, "f16"), (1, 7, 4, "f16"), (3, 7, 4, "f16"), (3, 11, 1, "f16"),
+                                          (1, 7, 4, "bf16"), (2, 7, 4, "f32")])
+def test_frm_implicit_start_equals_init_start(ddm, B, S, it, dtype):
     import torch
     from synth.torchio import to_device
-    D1n, D2n, dt = _maps(B, 500 + 10 * S + it)
+    sdt, tdt = {"f16": (synth.F16, torch.float16), "bf16": (synth.BF16, torch.bfloat16),
+                "f32": (synth.F32, torch.float32)}[dtype]
+    D1n, D2n, dt = _maps(B, 500 + 10 * S + it, sdt)
     D1 = torch.stack([to_device(a, dt, "cuda") for a in D1n])
     D2 = torch.stack([to_device(a, dt, "cuda") for a in D2n])
     if B == 1:
@@ -65,7 +68,7 @@ def test_frm_implicit_start_equals_init_start(ddm, B, S, it):
     seeds = oracle.seed_grid(100, 90, S)
     k = len(seeds)
     assert k % 16 != 0
-    buf = ddm.FrmBuffers(B, 100, 90, 96, 70, 24, torch.float16, S, it, D1.device)
+    buf = ddm.FrmBuffers(B, 100, 90, 96, 70, 24, tdt, S, it, D1.device)
     runs = []
     try:
         for what, mode, after, limit in STARTS:
