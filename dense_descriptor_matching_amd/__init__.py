@@ -16,6 +16,7 @@ Pixel indices are linear, p = x + W * y; :func:`to_xy` converts.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
 
@@ -76,7 +77,17 @@ def _declare(lib):
     lib.ddm_debug_set_output_bitmap_limit.argtypes = [I]; lib.ddm_debug_set_output_bitmap_limit.restype = I
     lib.ddm_profile_enable.argtypes = [I]; lib.ddm_profile_enable.restype = I
     lib.ddm_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]; lib.ddm_profile_read.restype = I
+    lib.ddm_release_cached_resources.argtypes = []; lib.ddm_release_cached_resources.restype = I
+    lib.ddm_frm_stats.argtypes = [P, I, I, I64, I64, P]; lib.ddm_frm_stats.restype = I
     return lib
+
+
+DDM_MAX_ITER = 64
+
+
+class FrmStats(C.Structure):
+    """ddm_stats: iterations run, active seeds per half-step, NN dot products."""
+    _fields_ = [("iters", C.c_int32), ("active", C.c_int32 * (2 * DDM_MAX_ITER)), ("dot_products", C.c_int64)]
 
 
 def lib():
@@ -87,7 +98,22 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
                                "(python -m dense_descriptor_matching_amd.build)")
         _lib = _declare(C.CDLL(LIB_PATH))
+        # The library's cached HIP graphs, capture streams and events are released while the
+        # HIP runtime is still up (interpreter exit runs before the runtime's own teardown).
+        atexit.register(_release_at_exit)
     return _lib
+
+
+def _release_at_exit():
+    if _lib is not None:
+        _lib.ddm_release_cached_resources()     # a failure this late has no one left to report to
+
+
+def release_cached_resources():
+    """Destroy the library's cached HIP graphs, capture streams and timing events (they are
+    recreated on demand). Runs at interpreter exit; callable any time no call is in flight."""
+    if _lib is not None:
+        _rc(_lib.ddm_release_cached_resources(), "ddm_release_cached_resources")
 
 
 def _ptr(t):
@@ -219,6 +245,20 @@ def nn(Q: torch.Tensor, R: torch.Tensor, q_rows: torch.Tensor | None = None, met
 
 
 # ------------------------------------------------------------------- FRM
+def frm_stats(query_counts, max_iter: int, N1: int, N2: int):
+    """ddm_stats of each pair from an FRM call's per-iteration query counts ([B * 2 * max_iter],
+    device or host; read after the call): list of dicts with iters, active (per half-step) and
+    dot_products."""
+    qc = torch.as_tensor(query_counts).to("cpu", torch.int32).contiguous()
+    B = qc.numel() // (2 * max_iter)
+    if B < 1 or qc.numel() != B * 2 * max_iter:
+        raise ValueError("query_counts must hold B * 2 * max_iter entries")
+    out = (FrmStats * B)()
+    _rc(lib().ddm_frm_stats(C.c_void_p(qc.data_ptr()), B, max_iter, N1, N2, C.cast(out, C.c_void_p)),
+        "ddm_frm_stats")
+    return [dict(iters=o.iters, active=list(o.active[:2 * max_iter]), dot_products=o.dot_products) for o in out]
+
+
 def _count(n) -> int:
     n = int(n)
     if n < 0:

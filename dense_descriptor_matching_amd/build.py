@@ -13,9 +13,10 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep MFMA results in architectural VGPRs: the epilogue reads every one of them
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-    # maxima of finite scores: no NaN canonicalisation around v_max3 (padding NaNs are quiet and
-    # v_max3_f32 returns the other operand, which the ragged-tail parity tests cover)
-    "-fno-honor-nans",
+    # device code only: scores are maxima of finite values (inputs are finite, padded reference
+    # slots hold copies of real rows, no NaN is ever formed), so v_max3 needs no NaN
+    # canonicalisation; host code keeps IEEE semantics
+    "-Xarch_device", "-fno-honor-nans",
     # no packed-fp32 instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

@@ -845,16 +845,45 @@ int effective_mode(int dev) {
 // exceeds their GPU time once the active set has shrunk. The sequence depends
 // only on the call's arguments, so it is captured once into a HIP graph on a
 // private capture stream, instantiated, cached (a few entries, most recently
-// used first) and replayed on the caller's stream with a single launch.
+// used first) and replayed on the caller's stream with a single launch. An
+// event recorded after every replay tells when the last replay of an entry has
+// finished, so an entry is destroyed (on eviction or release) only once its
+// work is done. The cache owns these objects; ddm_release_cached_resources
+// destroys them, which must happen before the HIP runtime shuts down.
 using GraphKey = std::array<uint64_t, 28>;
+
+struct GraphEntry {
+    GraphKey key;
+    hipGraphExec_t exec;
+    hipEvent_t done;      // recorded on the caller's stream after each replay
+};
 
 struct GraphCache {
     std::mutex mu;
-    std::list<std::pair<GraphKey, hipGraphExec_t>> lru;
+    std::list<GraphEntry> lru;
     std::vector<hipStream_t> cap;     // per device: private capture stream (default priority)
     static constexpr size_t kMax = 8;
 };
 GraphCache &graphs() { static GraphCache g; return g; }
+
+// Wait for the entry's last replay, then destroy its objects (on the entry's device).
+hipError_t destroy_entry(GraphEntry &e) {
+    int cur = 0;
+    hipError_t st = hipGetDevice(&cur);
+    const int dev = (int)e.key[0];
+    if (st == hipSuccess && dev != cur) st = hipSetDevice(dev);
+    auto keep = [&](hipError_t x) { if (st == hipSuccess) st = x; };
+    if (e.done) { keep(hipEventSynchronize(e.done)); keep(hipEventDestroy(e.done)); }
+    if (e.exec) keep(hipGraphExecDestroy(e.exec));
+    e.done = nullptr; e.exec = nullptr;
+    if (dev != cur) keep(hipSetDevice(cur));
+    return st;
+}
+
+int replay(GraphEntry &e, hipStream_t stream) {
+    if (hipGraphLaunch(e.exec, stream) != hipSuccess) return DDM_ERR_HIP;
+    return hipEventRecord(e.done, stream) == hipSuccess ? DDM_OK : DDM_ERR_HIP;
+}
 
 template <class Enqueue>
 int run_graphed(const GraphKey &key, hipStream_t stream, Enqueue enqueue) {
@@ -864,9 +893,9 @@ int run_graphed(const GraphKey &key, hipStream_t stream, Enqueue enqueue) {
     GraphCache &G = graphs();
     std::lock_guard<std::mutex> lock(G.mu);
     for (auto it = G.lru.begin(); it != G.lru.end(); ++it) {
-        if (it->first == key) {
+        if (it->key == key) {
             G.lru.splice(G.lru.begin(), G.lru, it);
-            return hipGraphLaunch(G.lru.front().second, stream) == hipSuccess ? DDM_OK : DDM_ERR_HIP;
+            return replay(G.lru.front(), stream);
         }
     }
     const int dev = (int)key[0];
@@ -881,16 +910,60 @@ int run_graphed(const GraphKey &key, hipStream_t stream, Enqueue enqueue) {
         if (graph) (void)hipGraphDestroy(graph);
         return rc != DDM_OK ? rc : DDM_ERR_HIP;
     }
-    hipGraphExec_t exec = nullptr;
-    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    GraphEntry e{key, nullptr, nullptr};
+    const hipError_t ei = hipGraphInstantiate(&e.exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (ei != hipSuccess) return DDM_ERR_HIP;
-    if (G.lru.size() >= GraphCache::kMax) {
-        (void)hipGraphExecDestroy(G.lru.back().second);
-        G.lru.pop_back();
+    if (hipEventCreateWithFlags(&e.done, hipEventDisableTiming) != hipSuccess) {
+        e.done = nullptr;
+        (void)destroy_entry(e);
+        return DDM_ERR_HIP;
     }
-    G.lru.emplace_front(key, exec);
-    return hipGraphLaunch(exec, stream) == hipSuccess ? DDM_OK : DDM_ERR_HIP;
+    if (G.lru.size() >= GraphCache::kMax) {
+        const hipError_t ed = destroy_entry(G.lru.back());
+        G.lru.pop_back();
+        if (ed != hipSuccess) { (void)destroy_entry(e); return DDM_ERR_HIP; }
+    }
+    G.lru.push_front(e);
+    return replay(G.lru.front(), stream);
+}
+
+// Destroy every cached graph, capture stream and timing event (the library
+// recreates them on demand).
+int release_cached() {
+    int rc = DDM_OK;
+    {
+        GraphCache &G = graphs();
+        std::lock_guard<std::mutex> lock(G.mu);
+        for (GraphEntry &e : G.lru)
+            if (destroy_entry(e) != hipSuccess) rc = DDM_ERR_HIP;
+        G.lru.clear();
+        // HIP is only called for objects that exist (a process that never launched makes no call)
+        const bool any_stream = std::any_of(G.cap.begin(), G.cap.end(), [](hipStream_t x) { return x != nullptr; });
+        if (any_stream) {
+            int cur = 0;
+            if (hipGetDevice(&cur) != hipSuccess) rc = DDM_ERR_HIP;
+            for (size_t dev = 0; dev < G.cap.size(); ++dev) {
+                if (!G.cap[dev]) continue;
+                if (hipSetDevice((int)dev) != hipSuccess || hipStreamSynchronize(G.cap[dev]) != hipSuccess ||
+                    hipStreamDestroy(G.cap[dev]) != hipSuccess)
+                    rc = DDM_ERR_HIP;
+                G.cap[dev] = nullptr;
+            }
+            if (hipSetDevice(cur) != hipSuccess) rc = DDM_ERR_HIP;
+        }
+    }
+    Profiler &P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    for (auto *v : {&P.pending, &P.pool}) {
+        for (auto &ev : *v) {
+            if (hipEventSynchronize(ev.second) != hipSuccess || hipEventDestroy(ev.first) != hipSuccess ||
+                hipEventDestroy(ev.second) != hipSuccess)
+                rc = DDM_ERR_HIP;
+        }
+        v->clear();
+    }
+    return rc;
 }
 
 }  // namespace
@@ -911,6 +984,28 @@ const char *ddm_status_str(int status) {
 }
 
 int64_t ddm_seed_count(int H, int W, int grid_stride) { return seed_count(H, W, grid_stride); }
+
+int ddm_frm_stats(const int32_t *qc, int B, int max_iter, int64_t N1, int64_t N2, ddm_stats *stats) {
+    if (!qc || !stats || B < 1 || max_iter < 1 || max_iter > DDM_MAX_ITER || N1 < 0 || N2 < 0)
+        return DDM_ERR_INVALID;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *c = qc + (size_t)b * 2 * max_iter;
+        for (int h = 0; h < 2 * max_iter; ++h)
+            if (c[h] < 0) return DDM_ERR_INVALID;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int32_t *c = qc + (size_t)b * 2 * max_iter;
+        ddm_stats &st = stats[b];
+        std::memset(&st, 0, sizeof(st));
+        for (int t = 0; t < max_iter; ++t) {
+            st.active[2 * t] = c[2 * t];
+            st.active[2 * t + 1] = c[2 * t + 1];
+            if (c[2 * t] > 0) st.iters = t + 1;
+            st.dot_products += (int64_t)c[2 * t] * N2 + (int64_t)c[2 * t + 1] * N1;
+        }
+    }
+    return DDM_OK;
+}
 
 int ddm_frm_set_mode(int mode) {
     if (mode != DDM_FRM_PER_HALF_STEP && mode != DDM_FRM_LOOP && mode != DDM_FRM_TAIL) return DDM_ERR_INVALID;
@@ -943,6 +1038,8 @@ int ddm_frm_set_barrier_polls(int polls) {
     loop_spin_limit().store(polls == 0 ? kSpinLimit : polls);
     return DDM_OK;
 }
+
+int ddm_release_cached_resources(void) { return release_cached(); }
 
 int ddm_profile_enable(int mask) {
     if (mask < 0 || mask > 3) return DDM_ERR_INVALID;
@@ -1043,7 +1140,12 @@ static int frm_entry(int B, const void *D1, int H1, int W1, const void *D2, int 
     FrmPlan P;
     if (O.starts && O.n_starts < 0) return DDM_ERR_INVALID;
     if (!O.starts && O.n_starts != 0) return DDM_ERR_INVALID;
-    if (!(O.pixel_tol >= 0.0) || !std::isfinite(O.pixel_tol)) return DDM_ERR_INVALID;
+    {
+        // finite and not negative, decided on the bits (NaN and infinities have an all-ones exponent)
+        uint64_t b;
+        std::memcpy(&b, &O.pixel_tol, sizeof(b));
+        if (((b >> 52) & 0x7ff) == 0x7ff || ((b >> 63) && (b << 1) != 0)) return DDM_ERR_INVALID;
+    }
     if (O.pixel_tol > 0.0 && !O.starts) return DDM_ERR_INVALID;       // the routine has no grid form of it
     int rc = frm_plan(B, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P, O.starts ? O.n_starts : -1, metric);
     if (rc) return rc;

@@ -209,7 +209,9 @@ __global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, const in
                           if (valid && sub == 0) {
                               const bool ok = !given || (given[x] >= 0 && given[x] < nrows);
                               out_idx[x] = ok ? j : -1;
-                              out_score[x] = ok ? reported(s, a.neg_out) : __builtin_nanf("");
+                              // the quiet-NaN pattern is stored as an integer: no floating-point NaN is formed
+                              reinterpret_cast<uint32_t *>(out_score)[x] =
+                                  ok ? __float_as_uint(reported(s, a.neg_out)) : 0x7fc00000u;
                           }
                       });
 }

@@ -33,9 +33,13 @@
 //   one ds_max_f32 per tile into an LDS column array (the four lanes that hold
 //   one column meet there), flushed once per workgroup as order-preserving keys.
 //
-// Invalid reference slots (chunk tail) hold NaN, whose scores are NaN and are
-// ignored by v_max3 (maxNum semantics); invalid query rows duplicate the last
-// valid row, which changes no column maximum and is never written back.
+// Reference slots past the end of the map (the tail of the last index group)
+// hold copies of the last valid reference: their scores repeat one of the
+// group's own scores, so no row maximum changes, and a tie with the original
+// resolves to the lower (group, slot), which is the original's (a copy's slot
+// index is never lower); their column maxima are not written. Query rows past
+// the query count repeat the last valid row, which changes no column maximum
+// and is never written back. No NaN or infinity ever enters a score.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -72,7 +76,6 @@ template <> struct Tr<DT_F16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
                                                       __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
     }
-    __device__ static raw nan_piece() { return raw{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u}; }
     __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
     __device__ static float elem(const unsigned char *p, int k) {
         return (float)reinterpret_cast<const _Float16 *>(p)[k];
@@ -85,7 +88,6 @@ template <> struct Tr<DT_BF16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     }
-    __device__ static raw nan_piece() { return raw{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}; }
     __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
     __device__ static float elem(const unsigned char *p, int k) {
         uint32_t u = (uint32_t)reinterpret_cast<const uint16_t *>(p)[k] << 16;
@@ -98,18 +100,11 @@ template <> struct Tr<DT_F32> {
     __device__ static f32x4_t mma(raw a, raw b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a), __uint_as_float(b), c, 0, 0, 0);
     }
-    __device__ static raw nan_piece() { return 0x7fc00000u; }
     __device__ static raw zero() { return 0u; }
     __device__ static float elem(const unsigned char *p, int k) {
         return reinterpret_cast<const float *>(p)[k];
     }
 };
-
-// 16-byte NaN pieces in device memory, the source of chunk slots past the end
-// of a map when the chunk is staged with direct-to-LDS loads.
-__device__ const uint32_t kNanPiece16[2][4] = {{0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u},
-                                               {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}};
-__device__ __forceinline__ const uint32_t *nan_piece16(int dt) { return kNanPiece16[dt == DT_BF16 ? 1 : 0]; }
 
 struct SweepArgs {
     const unsigned char *Q;      // query map of pair 0
@@ -459,15 +454,14 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
         // 16-byte pieces: global_load_lds_dwordx4 moves each lane's piece straight
         // into LDS at the wave's base + 16 * lane, so a wave fills 1 KB per
         // instruction with no register round trip, and every load of the chunk is
-        // in flight before the single wait. Slots past the map read a NaN piece.
+        // in flight before the single wait. Slots past the map read the last valid row.
         const int total = nslots * np;
         for (int base = wave * 64; base < total; base += NW * 64) {
             const int qq = base + lane;
             const int tile = qq / (np * 16), rem = qq - tile * (np * 16);
             const int pc = rem >> 4, c = rem & 15;
             const int r = (tile / G) * GROUP + G * c + tile % G;
-            const unsigned char *src = (r < nvalid) ? R + ((long long)(r0 + r) * p.ld + pc * E) * ESZ
-                                                    : reinterpret_cast<const unsigned char *>(nan_piece16(DT));
+            const unsigned char *src = R + ((long long)(r0 + min(r, nvalid - 1)) * p.ld + pc * E) * ESZ;
             if (qq < total)
                 __builtin_amdgcn_global_load_lds(
                     (const void __attribute__((address_space(1))) *)src,
@@ -486,9 +480,9 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
                 const int tile = qq / (np * 16), rem = qq - tile * (np * 16);
                 const int pc = rem >> 4, c = rem & 15;
                 const int r = (tile / G) * GROUP + G * c + tile % G;
-                v[u] = T::nan_piece();
-                if (qq < total && r < nvalid)
-                    v[u] = *reinterpret_cast<const raw *>(R + ((long long)(r0 + r) * p.ld + pc * E) * ESZ);
+                v[u] = T::zero();
+                if (qq < total)
+                    v[u] = *reinterpret_cast<const raw *>(R + ((long long)(r0 + min(r, nvalid - 1)) * p.ld + pc * E) * ESZ);
             }
 #pragma unroll
             for (int u = 0; u < SU; ++u) {

@@ -126,6 +126,22 @@ int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2
                   int32_t *seed_state, int32_t *query_counts,
                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Statistics of one FRM call, derived on the host from its query_counts (copied to host memory
+ * after the stream has passed the call; the call itself never waits for the device):
+ *   iters         iterations that ran, the last one with at least one forward query
+ *   active[2t]    seeds active in the forward half-step of iteration t+1 (= its forward queries),
+ *   active[2t+1]  seeds still active for its backward half-step; zero past iters
+ *   dot_products  sum over iterations of forward queries x N2 + backward queries x N1
+ * ddm_frm_stats fills stats[b] for each of B pairs from query_counts_host [B][2*max_iter].
+ * Returns DDM_ERR_INVALID for null pointers, B < 1, max_iter outside 1..DDM_MAX_ITER or negative
+ * sizes or counts. */
+typedef struct {
+    int32_t iters;
+    int32_t active[2 * DDM_MAX_ITER];
+    int64_t dot_products;
+} ddm_stats;
+int ddm_frm_stats(const int32_t *query_counts_host, int B, int max_iter, int64_t N1, int64_t N2, ddm_stats *stats);
+
 /* B independent pairs in one call: D1 is [B][H1][W1][d], D2 is [B][H2][W2][d].
  * Pair b writes its pairs at out_*[b * capacity ...] and its count at
  * out_count[b]; seed_state is [B][k][4] and query_counts [B][2*max_iter].
@@ -200,20 +216,20 @@ int ddm_frm_set_tail_after(int iterations);
 /* Test aid for the failure path of DDM_FRM_LOOP and DDM_FRM_TAIL: the number of polls a wait makes
  * before giving up (0 restores the default of 2^20, about 1 s). A tiny value makes the loop
  * kernel's barriers time out on purpose (and any tail-kernel wait that does not end at once); the
- * kernel still ends and out_count reads -1. Process-wide; graph-cached calls keep the value they
- * were recorded with. */
+ * kernel still ends and out_count reads -1. Process-wide; the value is part of the graph-cache
+ * key (a changed value records a new graph). */
 int ddm_frm_set_barrier_polls(int polls);
 /* Test aid against races between workgroups: caps the grid of the FRM sweep, update, loop and
  * tail kernels (which spread their tasks over whatever grid they get) at max_workgroups; 0 removes
  * the cap. Outputs must be bit-identical with any cap; 1 runs every task in one workgroup.
- * Process-wide; graph-cached calls keep the value they were recorded with. */
+ * Process-wide; the value is part of the graph-cache key (a changed value records a new graph). */
 int ddm_debug_set_grid_cap(int max_workgroups);
 /* Test aid for the two output paths of FRM: a call whose image 1 has at most max_pixels pixels (and
  * at most 4096 seeds per pair) collects and orders its pairs in one workgroup per pair through a
  * bitmap of image-1 pixels in LDS; larger ones use a collection kernel and a multi-workgroup
  * compaction of a dense match array. Both give identical outputs. -1 restores the default (2^19,
  * also the maximum); 0 sends every call down the multi-workgroup path. Process-wide;
- * graph-cached calls keep the value they were recorded with. DDM_ERR_INVALID below -1. */
+ * the value is part of the graph-cache key (a changed value records a new graph). DDM_ERR_INVALID below -1. */
 int ddm_debug_set_output_bitmap_limit(int max_pixels);
 
 /* ----------------------------------------------------- coarse-to-fine ---
@@ -278,6 +294,18 @@ int ddm_mutual_nn_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
  * and forgets them. Events are created on first use and kept for reuse. */
 int ddm_profile_enable(int mask);
 int ddm_profile_read(double *total_ms, int64_t *launches);
+
+/* ------------------------------------------------------------ resources ---
+ * Per process the library keeps the instantiated HIP graphs of recent FRM and
+ * coarse-to-fine calls (each with an event recorded after its latest replay), one
+ * private capture stream per device and the timing events of ddm_profile_enable.
+ * ddm_release_cached_resources waits until each cached graph's latest replay has
+ * finished, then destroys all of them; later calls recreate what they need. Call it
+ * while the HIP runtime is still up: before leaving main, before hipDeviceReset
+ * (the Python binding registers it to run at interpreter exit). It must not overlap
+ * another call into the library. Returns DDM_OK, or DDM_ERR_HIP if a HIP call failed
+ * (everything is released regardless). */
+int ddm_release_cached_resources(void);
 
 #ifdef __cplusplus
 }

@@ -103,5 +103,7 @@ int main(int argc, char **argv) {
                 ddm_status_str(frm.status), frm.count, mut.status, ddm_status_str(mut.status), mut.count);
     (void)hipFree(D1); (void)hipFree(D2); (void)hipFree(oi); (void)hipFree(oj); (void)hipFree(os);
     (void)hipFree(ocount); (void)hipFree(ws);
-    return frm.status == DDM_OK && mut.status == DDM_OK ? 0 : 1;
+    const int rel = ddm_release_cached_resources();     // the library's graphs, while HIP is still up
+    if (rel != DDM_OK) std::fprintf(stderr, "release: %s\n", ddm_status_str(rel));
+    return frm.status == DDM_OK && mut.status == DDM_OK && rel == DDM_OK ? 0 : 1;
 }

@@ -256,3 +256,22 @@ def test_c_abi_demo_is_built_and_links():
     assert os.path.exists(demo), "build with __graft_entry__.build()"
     r = subprocess.run([demo], capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "usage" in r.stderr
+
+
+def test_frm_stats_from_query_counts():
+    """ddm_stats from the per-iteration query counts (host-only; no device involved)."""
+    import dense_descriptor_matching_amd as ddm
+    qc = [3072, 3072, 700, 650, 40, 30, 0, 0, 0, 0,
+          5, 5, 0, 0, 0, 0, 0, 0, 0, 0]
+    st = ddm.frm_stats(qc, 5, 196608, 1000)
+    assert st[0]["iters"] == 3 and st[1]["iters"] == 1
+    assert st[0]["active"] == qc[:10] and st[1]["active"] == qc[10:]
+    assert st[0]["dot_products"] == (3072 + 700 + 40) * 1000 + (3072 + 650 + 30) * 196608
+    assert st[1]["dot_products"] == 5 * 1000 + 5 * 196608
+    L = ddm.lib()
+    import ctypes as C
+    bad = (C.c_int32 * 2)(1, -1)
+    out = ddm.FrmStats()
+    assert L.ddm_frm_stats(C.cast(bad, C.c_void_p), 1, 1, 10, 10, C.byref(out)) == -1
+    assert L.ddm_frm_stats(C.cast(bad, C.c_void_p), 1, 65, 10, 10, C.byref(out)) == -1
+    assert L.ddm_frm_stats(None, 1, 1, 10, 10, C.byref(out)) == -1
