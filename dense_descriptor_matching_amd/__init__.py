@@ -79,6 +79,8 @@ def _declare(lib):
     lib.ddm_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]; lib.ddm_profile_read.restype = I
     lib.ddm_release_cached_resources.argtypes = []; lib.ddm_release_cached_resources.restype = I
     lib.ddm_frm_stats.argtypes = [P, I, I, I64, I64, P]; lib.ddm_frm_stats.restype = I
+    lib.ddm_frm_match_noalloc.argtypes = [P, I, I, P, I, I, I, I, I, I, P, P, P, I, P, P, P, P]
+    lib.ddm_frm_match_noalloc.restype = I
     return lib
 
 

@@ -18,7 +18,27 @@
 
 using namespace ddm;
 
+// Workspace of ddm_frm_match_noalloc: library-held device memory, one copy per device, for the
+// life of the process. Host code never passes this name to a kernel (on the host it is only a
+// stand-in for the symbol); the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[DDM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on each device, looked up once per device with that device current.
+int scratch_ptr(int dev, void **out) {
+    static std::mutex mu;
+    static std::vector<void *> ptrs;
+    std::lock_guard<std::mutex> g(mu);
+    if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+    if (!ptrs[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DDM_ERR_HIP;
+        ptrs[dev] = ptr;
+    }
+    *out = ptrs[dev];
+    return DDM_OK;
+}
 
 // Sweep shapes. Each wave holds RQ query tiles of 16 rows. A workgroup keeps one
 // LDS-resident reference chunk and carries 8 waves (two per SIMD), so that one
@@ -261,11 +281,14 @@ struct Profiler {
 };
 Profiler &prof() { static Profiler p; return p; }
 
+// Set while ddm_frm_match_noalloc enqueues: no timing events are created or recorded.
+thread_local bool t_no_events = false;
+
 // Enqueue fn(), bracketed by two events on s when timing of `kind` is on.
 template <class Fn>
 hipError_t with_events(int kind, hipStream_t s, Fn fn) {
     Profiler &P = prof();
-    if (!(P.mask & kind)) return fn();
+    if (t_no_events || !(P.mask & kind)) return fn();
     std::pair<hipEvent_t, hipEvent_t> ev;
     {
         std::lock_guard<std::mutex> g(P.mu);
@@ -1184,6 +1207,33 @@ int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2
     return frm_entry(1, D1, H1, W1, D2, H2, W2, d, dtype, DDM_DOT, grid_stride, max_iter, FrmOpts{}, out_i, out_j,
                      out_score,
                      capacity, out_count, seed_state, query_counts, workspace, workspace_bytes, stream);
+}
+
+int ddm_frm_match_noalloc(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                          int grid_stride, int max_iter, int32_t *out_i, int32_t *out_j, float *out_score,
+                          int32_t capacity, int32_t *out_count, int32_t *seed_state, int32_t *query_counts,
+                          hipStream_t stream) {
+    FrmPlan P;
+    int rc = frm_plan(1, H1, W1, H2, W2, d, dtype, grid_stride, max_iter, &P);
+    if (rc) return rc;
+    if (!map_ok(D1, P.f) || !map_ok(D2, P.f)) return DDM_ERR_INVALID;
+    if (!out_i || !out_j || !out_score || !out_count) return DDM_ERR_INVALID;
+    if (capacity < P.k) return DDM_ERR_CAPACITY;
+    if (P.total > (size_t)DDM_NOALLOC_SCRATCH_BYTES) return DDM_ERR_WORKSPACE;   // before any HIP call
+    if (prepare_kernels() != hipSuccess) return DDM_ERR_HIP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DDM_ERR_HIP;
+    void *ws = nullptr;
+    rc = scratch_ptr(dev, &ws);
+    if (rc) return rc;
+    // direct launches (no graph is instantiated), no timing events, no cooperative launch: the loop
+    // mode runs as the tail mode, which gives the same bits
+    const int mode = effective_mode(dev) == DDM_FRM_LOOP ? DDM_FRM_TAIL : effective_mode(dev);
+    t_no_events = true;
+    rc = frm_run(P, FrmOpts{}, D1, D2, out_i, out_j, out_score, capacity, out_count, seed_state, query_counts, ws,
+                 stream, frm_exec(mode, P));
+    t_no_events = false;
+    return rc;
 }
 
 int ddm_frm_match_batched(int B, const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,

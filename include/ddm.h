@@ -126,6 +126,23 @@ int ddm_frm_match(const void *D1, int H1, int W1, const void *D2, int H2, int W2
                   int32_t *seed_state, int32_t *query_counts,
                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ddm_frm_match for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Same arguments, kernels and results as
+ * ddm_frm_match, without the workspace: the call uses a device array the library holds, one per
+ * device, DDM_NOALLOC_SCRATCH_BYTES in size, until the process ends. It calls no allocating
+ * routine and instantiates no graph (launches go straight onto `stream`, so they can be captured
+ * into the caller's graph); DDM_FRM_LOOP runs as DDM_FRM_TAIL (identical results) and no timing
+ * events are recorded. A problem whose ddm_frm_workspace_bytes(1, ...) exceeds
+ * DDM_NOALLOC_SCRATCH_BYTES is rejected with DDM_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one device shares that device's array and leaves its contents behind (each call
+ * initialises what it reads): calls that may overlap on one device (different streams, or
+ * threads) race and must be serialised by the caller. */
+#define DDM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ddm_frm_match_noalloc(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype,
+                          int grid_stride, int max_iter,
+                          int32_t *out_i, int32_t *out_j, float *out_score, int32_t capacity, int32_t *out_count,
+                          int32_t *seed_state, int32_t *query_counts, hipStream_t stream);
+
 /* Statistics of one FRM call, derived on the host from its query_counts (copied to host memory
  * after the stream has passed the call; the call itself never waits for the device):
  *   iters         iterations that ran, the last one with at least one forward query
