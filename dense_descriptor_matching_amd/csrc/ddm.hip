@@ -806,7 +806,7 @@ int c2f_run(const C2fPlan &P, const void *F1, const void *F2, int32_t *out_i, in
 struct MutualPlan {
     MapFmt f;
     int N1, N2, chunk, nchunks, sb_per_wg, qblocks, nblk;
-    size_t o_part, o_col, o_cmax, o_cfirst, o_owner, o_mj, o_ms, o_bc, o_bo, o_r1, o_r2, total;
+    size_t o_rowkey, o_colkey, o_owner, o_mj, o_ms, o_bc, o_bo, o_r1, o_r2, total;
 };
 
 int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p, int metric = DDM_DOT) {
@@ -827,10 +827,8 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p,
     p->qblocks = (nsb + p->sb_per_wg - 1) / p->sb_per_wg;
     p->nblk = (p->N1 + CB - 1) / CB;
     Bump b;
-    p->o_part = b.take((size_t)p->nchunks * p->N1 * 8);
-    p->o_col = b.take((size_t)p->qblocks * p->N2 * 4);
-    p->o_cmax = b.take((size_t)p->N2 * 4);
-    p->o_cfirst = b.take((size_t)p->N2 * 4);
+    p->o_rowkey = b.take((size_t)p->N1 * 8);
+    p->o_colkey = b.take((size_t)p->N2 * 8);
     p->o_owner = b.take((size_t)p->N2 * 4);
     p->o_mj = b.take((size_t)p->N1 * 4);
     p->o_ms = b.take((size_t)p->N1 * 4);
@@ -1334,28 +1332,27 @@ int ddm_mutual_nn_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
     if (rc) return rc;
     rc = maybe_repack(P.f, D2, P.N2, w + P.o_r2, stream, &m2, 1);
     if (rc) return rc;
+    uint64_t *rowkey = (uint64_t *)(w + P.o_rowkey), *colkey = (uint64_t *)(w + P.o_colkey);
+    int32_t *owner = (int32_t *)(w + P.o_owner);
+    hipLaunchKernelGGL(mutual_init_kernel, dim3((int)std::min<long long>((std::max(P.N1, P.N2) + 255) / 256, 2048)),
+                       dim3(256), 0, stream, rowkey, P.N1, colkey, owner, P.N2);
+    DDM_CHECK_LAUNCH();
     SweepArgs a{};
     a.Q = (const unsigned char *)m1; a.R = (const unsigned char *)m2;
-    a.rowpart = (uint64_t *)(w + P.o_part);
-    a.colpart = (uint32_t *)(w + P.o_col);
+    a.rowpart = rowkey;
+    a.colkey = colkey;
     a.nq = P.N1; a.nref = P.N2; a.ld = P.f.ld; a.chunk = P.chunk; a.nchunks = P.nchunks;
     a.sb_per_wg = P.sb_per_wg; a.rowcap = P.N1;
     DDM_CHECK(launch_sweep(P.f, true, a, dim3(P.nchunks, P.qblocks, 1), stream));
-    uint32_t *cmax = (uint32_t *)(w + P.o_cmax);
-    int32_t *cfirst = (int32_t *)(w + P.o_cfirst), *owner = (int32_t *)(w + P.o_owner);
-    hipLaunchKernelGGL(colmax_merge_kernel, dim3((P.N2 + 255) / 256), dim3(256), 0, stream,
-                       (const uint32_t *)a.colpart, P.qblocks, P.N2, cmax, cfirst, owner);
-    DDM_CHECK_LAUNCH();
     ResolveArgs ra{};
-    ra.rowpart = a.rowpart; ra.nchunks = P.nchunks; ra.rowcap = P.N1;
+    ra.rowpart = rowkey; ra.nchunks = 1; ra.rowcap = P.N1;
     ra.Q = a.Q; ra.nq = P.N1; ra.R = a.R; ra.nref = P.N2; ra.ld = P.f.ld; ra.d = P.f.d;
     ra.neg_out = P.f.l2 ? 1 : 0;
     int32_t *mj = (int32_t *)(w + P.o_mj);
     float *ms = (float *)(w + P.o_ms);
     const int qb = resolve_qb(P.N1);
     DDM_DT_QB_SWITCH(P.f.dtype, qb, mutual_rows_kernel, dim3((P.N1 + qb - 1) / qb), dim3(256), 0, stream, ra,
-                     (const uint32_t *)cmax, (const int32_t *)cfirst, P.sb_per_wg * P.f.sb_rows(), owner, mj, ms,
-                     nn12, s12);
+                     (const uint64_t *)colkey, P.sb_per_wg * P.f.sb_rows(), owner, mj, ms, nn12, s12);
     DDM_CHECK_LAUNCH();
     hipLaunchKernelGGL(mutual_claim_kernel, dim3(std::min((P.N1 + 255) / 256, 4096)), dim3(256), 0, stream,
                        (const int32_t *)owner, P.N1, mj);

@@ -217,39 +217,36 @@ __global__ void __launch_bounds__(256) nn_resolve_kernel(ResolveArgs a, const in
 }
 
 // ---------------------------------------------------------------------------
-// Mutual NN: column maxima over query blocks, then per row (i, j = NN_2(i)) is
+// Mutual NN: the fused sweep leaves one key per row (maximum, winning (group,
+// slot)) and one per column (maximum, first query block holding it), each
+// merged over the whole sweep by atomic maxima. Row i with j = NN_2(i) is
 // reciprocal iff column j's maximum equals row i's maximum (both are the same
-// matrix-core value, compared as order-preserving keys) and no lower row
-// reaches that maximum too (NN_1 takes the lowest index on ties). Lower rows
-// of earlier query blocks are excluded by the first block whose partial holds
-// the maximum; among the rows that pass, the lowest claims the column.
+// matrix-core value, compared as order-preserving keys) and no lower row reaches
+// that maximum too (NN_1 takes the lowest index on ties). Lower rows of earlier
+// query blocks are excluded by the column's first block; among the rows that
+// pass, the lowest claims the column.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) colmax_merge_kernel(const uint32_t *colpart, int nqblk, int nref,
-                                                           uint32_t *colmax, int32_t *colfirst, int32_t *owner) {
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= nref) return;
-    uint32_t m = 0;
-    int first = 0;
-    for (int b = 0; b < nqblk; ++b) {
-        const uint32_t v = colpart[(long long)b * nref + j];
-        if (v > m) { m = v; first = b; }
+// Clears the merged keys (0 loses to every real key) and the column owners.
+__global__ void __launch_bounds__(256) mutual_init_kernel(uint64_t *rowkey, int n1, uint64_t *colkey, int32_t *owner,
+                                                          int n2) {
+    for (int x = blockIdx.x * 256 + threadIdx.x; x < n1 || x < n2; x += gridDim.x * 256) {
+        if (x < n1) rowkey[x] = 0;
+        if (x < n2) { colkey[x] = 0; owner[x] = 0x7fffffff; }
     }
-    colmax[j] = m;
-    colfirst[j] = first;
-    owner[j] = 0x7fffffff;
 }
 
 template <int DT, int QB>
-__global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint32_t *colmax,
-                                                          const int32_t *colfirst, int rows_per_qblk, int32_t *owner,
-                                                          int32_t *match_j, float *match_s, int32_t *nn12,
-                                                          float *s12) {
+__global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint64_t *colkey, int rows_per_qblk,
+                                                          int32_t *owner, int32_t *match_j, float *match_s,
+                                                          int32_t *nn12, float *s12) {
     __shared__ uint64_t red[256];
     resolve_block<DT, QB, 256>(blockIdx.x, red, a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
                       [&](int x) { return a.Q + (long long)x * a.ld * Tr<DT>::ESZ; },
                       [&](bool valid, int x, int j, float s, int sub) {
                           if (valid && sub == 0) {
-                              const bool cand = colmax[j] == fkey(s) && x / rows_per_qblk == colfirst[j];
+                              const uint64_t ck = colkey[j];
+                              const bool cand = (uint32_t)(ck >> 32) == fkey(s) &&
+                                                (uint32_t)(x / rows_per_qblk) == ~(uint32_t)ck;
                               if (cand) atomicMin(owner + j, x);
                               const float rs = reported(s, a.neg_out);
                               match_j[x] = cand ? j : -1;

@@ -111,10 +111,13 @@ struct SweepArgs {
     const unsigned char *R;      // reference map of pair 0
     const int32_t *qrows;        // optional gather list (row of Q for each query)
     const int32_t *qcount;       // optional device query count (else nq)
-    uint64_t *rowpart;           // [pair][nchunks][rowcap] row partial keys
-    uint32_t *colpart;           // [pair][nqblk][nref] column partial keys (COLMAX)
+    uint64_t *rowpart;           // [pair][nchunks][rowcap] row partial keys; COLMAX: [nq] row keys merged
+                                 // by atomic maximum over all chunks
+    uint64_t *colkey;            // COLMAX: [nref] column keys merged by atomic maximum over all query
+                                 // blocks: high word = order-preserving key of the column maximum,
+                                 // low word = ~(first query block holding it)
     long long q_bs, r_bs;        // bytes between pairs
-    long long qrows_bs, qcount_bs, rowpart_bs, colpart_bs;   // elements between pairs
+    long long qrows_bs, qcount_bs, rowpart_bs;   // elements between pairs
     int nq;                      // query count (upper bound when qcount is set)
     int nref;                    // reference rows per pair
     int ld;                      // row stride in elements
@@ -361,7 +364,10 @@ __device__ __forceinline__ void sweep_rows(const SweepArgs &p, const unsigned ch
         }
     }
 
-    // ---- row flush: max over the 16 slots of each row, lowest (group, slot) among equals
+    // ---- row flush: max over the 16 slots of each row, lowest (group, slot) among equals. Every
+    // key is computed first, without branches, so the independent DPP chains of all registers
+    // can interleave; the stores follow.
+    uint64_t key[RQ][4];
 #pragma unroll
     for (int qt = 0; qt < RQ; ++qt)
 #pragma unroll
@@ -369,10 +375,22 @@ __device__ __forceinline__ void sweep_rows(const SweepArgs &p, const unsigned ch
             const float bv = bA[qt][r];
             const float m = row16_max(bv);
             const uint32_t id = ((gbase + (uint32_t)gid[qt][r]) << 4) | (uint32_t)c;
-            const uint32_t cand = row16_min(bv == m ? id : 0xffffffffu);
-            const int row = row_of(qt) + 4 * g + r;
-            if (c == 0 && row < nq) rp[row] = row_key(m, cand);
+            key[qt][r] = row_key(m, row16_min(bv == m ? id : 0xffffffffu));
         }
+    if (c == 0) {
+#pragma unroll
+        for (int qt = 0; qt < RQ; ++qt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = row_of(qt) + 4 * g + r;
+                if (row < nq) {
+                    if constexpr (COLMAX)     // one key per row, merged over the chunks
+                        __hip_atomic_fetch_max(rp + row, key[qt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        rp[row] = key[qt][r];
+                }
+            }
+    }
 }
 
 // sweep_rows with as few query tiles per wave as the sub-block needs (tpw = 16-row
@@ -425,7 +443,8 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
     const int sb_first = qb * spw;
     if (sb_first >= n_sb) return;
     const int sb_last = min(sb_first + spw, n_sb);
-    uint64_t *rp = p.rowpart + pair * p.rowpart_bs + (long long)(chunk_id * sg.s + sub) * sg.rowcap;
+    uint64_t *rp = COLMAX ? p.rowpart + pair * p.rowpart_bs
+                          : p.rowpart + pair * p.rowpart_bs + (long long)(chunk_id * sg.s + sub) * sg.rowcap;
 
     const unsigned char *Q = p.Q + pair * p.q_bs;
     const unsigned char *R = p.R + pair * p.r_bs;
@@ -517,11 +536,16 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
 
     if constexpr (COLMAX) {
         __syncthreads();
-        uint32_t *cp = p.colpart + pair * p.colpart_bs + (long long)qblk * p.nref + r0;
+        // column maxima of this query block, merged into the column keys: the larger maximum wins,
+        // the lower query block among equal maxima (its complement is the larger low word)
+        uint64_t *ck = p.colkey + r0;
+        const uint64_t low = (uint64_t)(~(uint32_t)qblk);
         for (int s = tid; s < nslots; s += NW * 64) {
             const int tile = s / TILE, slot = s % TILE;
             const int r = (tile / G) * GROUP + slot * G + (tile % G);
-            if (r < nvalid) cp[r] = fkey(colmax_lds[s]);
+            if (r < nvalid)
+                __hip_atomic_fetch_max(ck + r, ((uint64_t)fkey(colmax_lds[s]) << 32) | low, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

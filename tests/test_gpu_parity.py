@@ -190,6 +190,31 @@ def test_mutual_matches_oracle(ddm, case):
     check_mutual(A, B, i.cpu().numpy(), j.cpu().numpy(), s.cpu().numpy())
 
 
+# ragged sizes: query counts just past a sub-block, reference counts just past / short of an index
+# group and a chunk, several K blocks, a single reference
+MUTUAL_RAGGED_CASES = [
+    (1, 769, 41, 25, 24, synth.F16, 11),      # 769 rows: one past a 768-row sub-block; 1025 references
+    (32, 32, 32, 32, 24, synth.F16, 12),
+    (17, 61, 3, 341, 16, synth.BF16, 13),     # 1037 rows, 1023 references
+    (45, 47, 45, 47, 64, synth.BF16, 14),     # d = 64: two K blocks
+    (20, 26, 50, 62, 48, synth.F16, 15),
+    (9, 9, 1, 1, 8, synth.F16, 16),           # one reference
+]
+
+
+@pytest.mark.parametrize("case", MUTUAL_RAGGED_CASES,
+                         ids=lambda c: f"{c[0]}x{c[1]}-{c[2]}x{c[3]}x{c[4]}-{synth.DTYPE_NAMES[c[5]]}")
+def test_mutual_ragged_sizes_match_oracle(ddm, case):
+    """The fused mutual pass at ragged sizes meets the oracle under R1 (row NN table) and R2."""
+    H1, W1, H2, W2, d, dt, seed = case
+    D1 = synth.random_map(H1, W1, d, dt, 1900 + seed)
+    D2 = synth.random_map(H2, W2, d, dt, 1950 + seed)
+    i, j, s, nn12, s12 = ddm.mutual_nn(dev(D1, dt), dev(D2, dt), return_nn=True)
+    A, B = dec(D1, dt), dec(D2, dt)
+    check_nn(A, B, None, nn12.cpu().numpy(), s12.cpu().numpy())
+    check_mutual(A, B, i.cpu().numpy(), j.cpu().numpy(), s.cpu().numpy())
+
+
 def test_mutual_shifted_pair_dense_matches(ddm):
     p = synth.make_pair(96, 64, 24, synth.F16, 77, sigma=0.05, shift=(3, -2))
     i, j, s = ddm.mutual_nn(dev(p.D1, synth.F16), dev(p.D2, synth.F16))
