@@ -275,3 +275,12 @@ def test_frm_stats_from_query_counts():
     assert L.ddm_frm_stats(C.cast(bad, C.c_void_p), 1, 1, 10, 10, C.byref(out)) == -1
     assert L.ddm_frm_stats(C.cast(bad, C.c_void_p), 1, 65, 10, 10, C.byref(out)) == -1
     assert L.ddm_frm_stats(None, 1, 1, 10, 10, C.byref(out)) == -1
+
+
+def test_mutual_workspace_is_linear_in_the_pixel_counts(L):
+    """The mutual pass keeps one merged key per row and per column: its workspace grows with N1 + N2,
+    not with N1 x N2 / chunk (28 bytes per pixel of a square pair, plus block counts and alignment)."""
+    for H, W in ((512, 384), (1024, 768), (2048, 1536)):
+        n = H * W
+        b = L.ddm_mutual_workspace_bytes(H, W, H, W, 24, 1)
+        assert 28 * n <= b <= 28 * n + n // 16 + 4096, (H, W, b)
