@@ -99,15 +99,18 @@ struct Bump {
     size_t take(size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; }
 };
 
+// LDS of a sweep task past the chunk (and COLMAX's column array): the unit counter
+constexpr size_t SWEEP_LDS_EXTRA = 16;
+
 int chunk_limit(const MapFmt &f, bool colmax, size_t lds_max = LDS_MAX) {
     const size_t per_ref = (size_t)f.tile_bytes() / TILE + (colmax ? 4 : 0);
     const int grp = f.group();
-    int c = (int)(lds_max / per_ref) / grp * grp;
+    int c = (int)((lds_max - SWEEP_LDS_EXTRA) / per_ref) / grp * grp;
     return std::max(c, grp);
 }
 
 size_t sweep_lds(const MapFmt &f, int chunk, bool colmax) {
-    return (size_t)(chunk / TILE) * f.tile_bytes() + (colmax ? (size_t)chunk * 4 : 0);
+    return (size_t)(chunk / TILE) * f.tile_bytes() + (colmax ? (size_t)chunk * 4 : 0) + SWEEP_LDS_EXTRA;
 }
 
 // ----------------------------------------------------------------- dispatch

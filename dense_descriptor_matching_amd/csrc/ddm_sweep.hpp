@@ -13,11 +13,14 @@
 //   grid.y  = query block (sb_per_wg sub-blocks of NW*RQ*16 rows)
 //   grid.z  = independent pair (batched calls)
 //   (The FRM kernels enumerate the same tasks from device counts instead.)
-//   In a sub-block, wave w keeps the 16-row query tiles w, w + NW, ... (RQ of
-//   them, fewer when the sub-block is short) resident in VGPRs as MFMA A
-//   operands and streams the chunk's 16-row reference tiles from LDS as B
-//   operands with v_mfma_f32_16x16x32_{f16,bf16} (v_mfma_f32_16x16x4_f32 for
-//   fp32 maps), K padded to 32 with zeros in A only.
+//   A sub-block has NW query slots; slot w is the 16-row query tiles w, w + NW,
+//   ... (RQ of them, fewer when the sub-block is short). The waves of a
+//   workgroup take (sub-block, slot) units from an LDS counter, so a wave that
+//   the SIMD's issue favours takes more of them and both waves of a SIMD
+//   finish together; a unit's tiles stay resident in VGPRs as MFMA A operands
+//   while the chunk's 16-row reference tiles stream from LDS as B operands
+//   with v_mfma_f32_16x16x32_{f16,bf16} (v_mfma_f32_16x16x4_f32 for fp32
+//   maps), K padded to 32 with zeros in A only.
 //
 // Epilogue (the part that bounds this kernel at d = 24)
 //   MFMA output lane l holds reference slot c = l % 16 and query rows
@@ -197,22 +200,21 @@ __device__ __forceinline__ uint32_t row16_min(uint32_t x) {
     return x;
 }
 
-// Queries of one sub-block against the staged chunk. Wave w takes the
-// sub-block's 16-row tiles w, w + NW, ..., RQ of them; rows past the query
-// count repeat the last valid row (no column maximum changes) and are not
-// written back.
+// Queries of one unit against the staged chunk: the sub-block's 16-row tiles
+// ws, ws + NW, ..., RQ of them; rows past the query count repeat the last
+// valid row (no column maximum changes) and are not written back.
 template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
 __device__ __forceinline__ void sweep_rows(const SweepArgs &p, const unsigned char *Q, const int32_t *qrows, int nq,
-                                           int sb_row0, int np, int TB, int nkb, int ngroups,
+                                           int sb_row0, int ws, int np, int TB, int nkb, int ngroups,
                                            const int (&boff)[NKB], uint32_t gbase, uint64_t *rp, float *colmax_lds,
                                            const unsigned char *lds) {
     constexpr int G = group_tiles(DT);
     using T = Tr<DT>;
     using raw = typename T::raw;
     constexpr int PS = T::PS, ESZ = T::ESZ;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int c = lane & 15, g = lane >> 4;
-    auto row_of = [&](int qt) { return sb_row0 + (wave + qt * NW) * 16; };
+    auto row_of = [&](int qt) { return sb_row0 + (ws + qt * NW) * 16; };
 
     raw a[RQ][NKB];
 #pragma unroll
@@ -393,16 +395,17 @@ __device__ __forceinline__ void sweep_rows(const SweepArgs &p, const unsigned ch
     }
 }
 
-// sweep_rows with as few query tiles per wave as the sub-block needs (tpw = 16-row
-// tiles of the busiest wave): a half-step with few active queries costs a
+// sweep_rows with as few query tiles per unit as the sub-block needs (tpw = 16-row
+// tiles of its fullest slot): a half-step with few active queries costs a
 // fraction of a full one. The fused column-maximum sweep always takes RQ.
 template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
 __device__ __forceinline__ void sweep_rows_fit(int tpw, const SweepArgs &p, const unsigned char *Q,
-                                               const int32_t *qrows, int nq, int sb_row0, int np, int TB, int nkb,
+                                               const int32_t *qrows, int nq, int sb_row0, int ws, int np, int TB,
+                                               int nkb,
                                                int ngroups, const int (&boff)[NKB], uint32_t gbase, uint64_t *rp,
                                                float *colmax_lds, const unsigned char *lds) {
 #define DDM_SWEEP_ROWS(RQV) \
-    sweep_rows<DT, NP, NKB, RQV, NW, COLMAX>(p, Q, qrows, nq, sb_row0, np, TB, nkb, ngroups, boff, gbase, rp, \
+    sweep_rows<DT, NP, NKB, RQV, NW, COLMAX>(p, Q, qrows, nq, sb_row0, ws, np, TB, nkb, ngroups, boff, gbase, rp, \
                                              colmax_lds, lds)
     if constexpr (COLMAX) {
         DDM_SWEEP_ROWS(RQ);
@@ -418,8 +421,9 @@ __device__ __forceinline__ void sweep_rows_fit(int tpw, const SweepArgs &p, cons
 // NP = pieces (of E elements) per stored row; 0 = runtime (fp32 path).
 // NKB = 32-wide (fp16/bf16) or 4-wide (fp32) K blocks.
 // One workgroup task: reference chunk chunk_id of pair `pair` against query
-// block qblk. The caller owns the LDS (at least sweep_lds bytes) and makes sure
-// no wave still reads it from a previous task.
+// block qblk. The caller owns the LDS (at least sweep_lds bytes: the staged
+// chunk, COLMAX's column array, the unit counter) and makes sure no wave still
+// reads it from a previous task.
 template <int DT, int NP, int NKB, int RQ, int NW, bool COLMAX>
 __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chunk_id, int qblk, unsigned char *lds)
 {
@@ -512,9 +516,11 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
         }
     }
     float *colmax_lds = reinterpret_cast<float *>(lds + (size_t)(p.chunk / TILE) * TB);
+    int *next_unit = reinterpret_cast<int *>(lds + (size_t)(p.chunk / TILE) * TB + (COLMAX ? (size_t)p.chunk * 4 : 0));
     if constexpr (COLMAX) {
         for (int s = tid; s < nslots; s += NW * 64) colmax_lds[s] = -INFINITY;
     }
+    if (tid == 0) *next_unit = NW;
     __syncthreads();
 
     const int c = lane & 15, g = lane >> 4;
@@ -526,12 +532,21 @@ __device__ __forceinline__ void sweep_task(const SweepArgs &p, int pair, int chu
     }
     const uint32_t gbase = (uint32_t)(r0 / GROUP);
 
-    for (int sb = sb_first; sb < sb_last; ++sb) {
-        const int sb_row0 = sb * SB_ROWS;
+    // units u = (sub-block sb_first + u / NW, slot u % NW): wave w starts with unit w, the later ones
+    // go in order to whichever wave asks next (no counter traffic when a task has one sub-block); a
+    // unit's rows and results do not depend on the wave that runs it
+    const int units = (sb_last - sb_first) * NW;
+    int u = __builtin_amdgcn_readfirstlane(wave);     // uniform over the wave: scalar unit arithmetic
+    while (u < units) {
+        const int sb_row0 = (sb_first + u / NW) * SB_ROWS, ws = u % NW;
         const int tiles = (min(SB_ROWS, nq - sb_row0) + 15) / 16;     // 16-row tiles holding queries
-        if (wave >= tiles) break;
-        sweep_rows_fit<DT, NP, NKB, RQ, NW, COLMAX>((tiles + NW - 1) / NW, p, Q, qrows, nq, sb_row0, np, TB, nkb,
-                                                    ngroups, boff, gbase, rp, colmax_lds, lds);
+        if (ws < tiles)
+            sweep_rows_fit<DT, NP, NKB, RQ, NW, COLMAX>((tiles + NW - 1) / NW, p, Q, qrows, nq, sb_row0, ws, np,
+                                                        TB, nkb, ngroups, boff, gbase, rp, colmax_lds, lds);
+        if (units <= NW) break;
+        int next = 0;
+        if (lane == 0) next = atomicAdd(next_unit, 1);
+        u = __builtin_amdgcn_readfirstlane(next);       // lane 0's value: every lane is active here
     }
 
     if constexpr (COLMAX) {
