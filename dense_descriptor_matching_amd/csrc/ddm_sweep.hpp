@@ -32,7 +32,7 @@
 //   (group, slot) are contiguous, and (group, slot, t) order equals reference
 //   order, so the lowest-index tie-break survives. The exact index inside the
 //   group is recovered later by recomputing 32 candidate dots (resolve_one).
-//   Column direction (COLMAX): in-lane v_max3 chain over the wave's rows, then
+//   Column direction (COLMAX): in-lane v_max3 chain over the unit's rows, then
 //   one ds_max_f32 per tile into an LDS column array (the four lanes that hold
 //   one column meet there), flushed once per workgroup as order-preserving keys.
 //
@@ -264,7 +264,7 @@ __device__ __forceinline__ void sweep_rows(const SweepArgs &p, const unsigned ch
     };
     // Row state: running maximum of each (row, slot) over the group's tiles,
     // v_max3 consumes one score of each tile of the pair. Columns: in-lane
-    // maximum over the wave's rows, one LDS float-max per tile (the four
+    // maximum over the unit's rows, one LDS float-max per tile (the four
     // lanes of a column, one per row group, meet in LDS).
     auto epi_pair = [&](const f32x4_t (&c0)[RQ], const f32x4_t (&c1)[RQ], int tile, bool first,
                         float (&bin)[RQ][4], float (&bout)[RQ][4]) __attribute__((always_inline)) {
