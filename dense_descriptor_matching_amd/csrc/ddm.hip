@@ -825,8 +825,9 @@ int mutual_plan(int H1, int W1, int H2, int W2, int d, int dtype, MutualPlan *p,
     p->chunk = chunk;
     p->nchunks = (p->N2 + chunk - 1) / chunk;
     // query sub-blocks per workgroup: aim at ~512 workgroups (two rounds of one workgroup per CU). Longer
-    // workgroups merge fewer column keys (one atomic per column and query block); measured at 512x384:
-    // 8 query blocks 2.185 ms, 16 or 32 (2048 workgroups) 2.21 ms
+    // workgroups merge fewer column keys (one atomic per column and query block) and spread the last unit's
+    // tail over more work; sweep at 512x384 on one machine: 4 query blocks 2.065 ms, 8 2.07-2.08, 64 2.23,
+    // 256 2.57
     const long long want_qblocks = std::max<long long>(1, 512 / p->nchunks);
     p->sb_per_wg = (int)std::max<long long>(1, (nsb + want_qblocks - 1) / want_qblocks);
     p->qblocks = (nsb + p->sb_per_wg - 1) / p->sb_per_wg;

@@ -215,6 +215,19 @@ def test_mutual_ragged_sizes_match_oracle(ddm, case):
     check_mutual(A, B, i.cpu().numpy(), j.cpu().numpy(), s.cpu().numpy())
 
 
+def test_mutual_several_sub_blocks_per_workgroup(ddm):
+    """Workgroups that sweep several 768-row sub-blocks hand their (sub-block, query slot) units out through a
+    counter: 6952 = 9 x 768 + 40 rows against 64 reference chunks of 3072 gives five query blocks of two
+    sub-blocks each, and the last sub-block's 40 rows (three 16-row tiles) leave five of its eight slots empty."""
+    H1, W1, H2, W2, d, dt = 79, 88, 512, 384, 24, synth.F16
+    D1 = synth.random_map(H1, W1, d, dt, 2101)
+    D2 = synth.random_map(H2, W2, d, dt, 2102)
+    i, j, s, nn12, s12 = ddm.mutual_nn(dev(D1, dt), dev(D2, dt), return_nn=True)
+    A, B = dec(D1, dt), dec(D2, dt)
+    check_nn(A, B, None, nn12.cpu().numpy(), s12.cpu().numpy())
+    check_mutual(A, B, i.cpu().numpy(), j.cpu().numpy(), s.cpu().numpy())
+
+
 def test_mutual_shifted_pair_dense_matches(ddm):
     p = synth.make_pair(96, 64, 24, synth.F16, 77, sigma=0.05, shift=(3, -2))
     i, j, s = ddm.mutual_nn(dev(p.D1, synth.F16), dev(p.D2, synth.F16))
