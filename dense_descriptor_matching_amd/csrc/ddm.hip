@@ -508,14 +508,14 @@ int frm_plan(int B, int H1, int W1, int H2, int W2, int d, int dtype, int S, int
 
 int compact_run(const int32_t *mj, const float *ms, long long n_bs, int n, int B, int nblk, int32_t *bc, int32_t *bo,
                 int32_t *out_i, int32_t *out_j, float *out_s, long long out_bs, int32_t *out_count, hipStream_t s,
-                const int32_t *err = nullptr) {
-    hipLaunchKernelGGL(compact_count_kernel, dim3(nblk, B), dim3(256), 0, s, mj, n_bs, n, bc, nblk);
+                const int32_t *err = nullptr, const int32_t *owner = nullptr) {
+    hipLaunchKernelGGL(compact_count_kernel, dim3(nblk, B), dim3(256), 0, s, mj, n_bs, n, bc, nblk, owner);
     DDM_CHECK_LAUNCH();
     hipLaunchKernelGGL(compact_scan_kernel, dim3(B), dim3(256), 0, s, (const int32_t *)bc, bo, nblk, out_count,
                        (int)out_bs, err);
     DDM_CHECK_LAUNCH();
     hipLaunchKernelGGL(compact_scatter_kernel, dim3(nblk, B), dim3(256), 0, s, mj, ms, n_bs, n,
-                       (const int32_t *)bo, nblk, out_i, out_j, out_s, out_bs, (int)out_bs);
+                       (const int32_t *)bo, nblk, out_i, out_j, out_s, out_bs, (int)out_bs, owner);
     DDM_CHECK_LAUNCH();
     return DDM_OK;
 }
@@ -1360,11 +1360,9 @@ int ddm_mutual_nn_ex(const void *D1, int H1, int W1, const void *D2, int H2, int
     DDM_DT_QB_SWITCH(P.f.dtype, qb, mutual_rows_kernel, dim3((P.N1 + qb - 1) / qb), dim3(256), 0, stream, ra,
                      (const uint64_t *)colkey, P.sb_per_wg * P.f.sb_rows(), owner, mj, ms, nn12, s12);
     DDM_CHECK_LAUNCH();
-    hipLaunchKernelGGL(mutual_claim_kernel, dim3(std::min((P.N1 + 255) / 256, 4096)), dim3(256), 0, stream,
-                       (const int32_t *)owner, P.N1, mj);
-    DDM_CHECK_LAUNCH();
+    // rows that lost their column's claim to a lower row drop out in the compaction
     return compact_run(mj, ms, P.N1, P.N1, 1, P.nblk, (int32_t *)(w + P.o_bc), (int32_t *)(w + P.o_bo), out_i, out_j,
-                       out_score, capacity, out_count, stream);
+                       out_score, capacity, out_count, stream, nullptr, (const int32_t *)owner);
 }
 
 int ddm_mutual_nn(const void *D1, int H1, int W1, const void *D2, int H2, int W2, int d, int dtype, int32_t *out_i,

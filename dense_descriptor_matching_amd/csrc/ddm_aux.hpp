@@ -235,32 +235,58 @@ __global__ void __launch_bounds__(256) mutual_init_kernel(uint64_t *rowkey, int 
     }
 }
 
+// One row per 16 lanes, QB rows per block in rounds of 16; the row key is the
+// merged one (one slot per row). A row can only pass when one of the G
+// candidates of its winning (group, slot) carries, in its column key, this
+// row's maximum and this row's query block; a row with no such candidate skips
+// the rescan (unless the caller asked for every row's NN) and is written as a
+// non-match. Rows that pass claim their column with an atomic minimum; the
+// compaction keeps a row only if it holds its column's claim.
 template <int DT, int QB>
 __global__ void __launch_bounds__(256) mutual_rows_kernel(ResolveArgs a, const uint64_t *colkey, int rows_per_qblk,
                                                           int32_t *owner, int32_t *match_j, float *match_s,
                                                           int32_t *nn12, float *s12) {
-    __shared__ uint64_t red[256];
-    resolve_block<DT, QB, 256>(blockIdx.x, red, a.rowpart, a.nchunks, a.rowcap, a.nq, a.R, a.nref, a.ld, a.d,
-                      [&](int x) { return a.Q + (long long)x * a.ld * Tr<DT>::ESZ; },
-                      [&](bool valid, int x, int j, float s, int sub) {
-                          if (valid && sub == 0) {
-                              const uint64_t ck = colkey[j];
-                              const bool cand = (uint32_t)(ck >> 32) == fkey(s) &&
-                                                (uint32_t)(x / rows_per_qblk) == ~(uint32_t)ck;
-                              if (cand) atomicMin(owner + j, x);
-                              const float rs = reported(s, a.neg_out);
-                              match_j[x] = cand ? j : -1;
-                              match_s[x] = rs;
-                              if (nn12) { nn12[x] = j; s12[x] = rs; }
-                          }
-                      });
-}
-
-// Rows that passed the test but lost their column to a lower row drop out.
-__global__ void __launch_bounds__(256) mutual_claim_kernel(const int32_t *owner, int n, int32_t *match_j) {
-    for (int x = blockIdx.x * 256 + threadIdx.x; x < n; x += gridDim.x * 256) {
-        const int j = match_j[x];
-        if (j >= 0 && owner[j] != x) match_j[x] = -1;
+    static_assert(QB % 16 == 0, "rounds of 16 rows");
+    constexpr int G = group_tiles(DT), GROUP = TILE * G;
+    const int sub = (int)threadIdx.x & 15, lane = (int)threadIdx.x & 63;
+#pragma unroll 1
+    for (int round = 0; round < QB / 16; ++round) {
+        const int x = (int)blockIdx.x * QB + round * 16 + (int)(threadIdx.x >> 4);
+        const bool valid = x < a.nq;                 // the same for the row's 16 lanes
+        uint64_t k = 0;
+        bool hit = false;
+        if (valid) {
+            k = a.rowpart[x];
+            const uint32_t id = ~(uint32_t)k, fk = (uint32_t)(k >> 32);
+            const uint32_t qlow = ~(uint32_t)(x / rows_per_qblk);
+            const int j0 = (int)((id >> 4) * GROUP + (id & 15u) * G);
+            for (int t = sub; t < G; t += 16) {
+                const int j = j0 + t;
+                if (j < a.nref) {
+                    const uint64_t ck = colkey[j];
+                    hit |= (uint32_t)(ck >> 32) == fk && (uint32_t)ck == qlow;
+                }
+            }
+        }
+        // any candidate of the row: its 16 lanes are one 16-bit field of the wave's ballot
+        hit = ((__ballot(hit) >> (lane & 48)) & 0xffffull) != 0;
+        if (!valid) continue;
+        int j = -1;
+        float s = fkey_inv((uint32_t)(k >> 32));
+        if (hit || nn12)
+            rescan_one<DT>(k, a.Q + (long long)x * a.ld * Tr<DT>::ESZ, a.R, a.nref, a.ld, a.d, sub, &j, &s);
+        if (sub == 0) {
+            bool cand = false;
+            if (hit) {
+                const uint64_t ck = colkey[j];
+                cand = (uint32_t)(ck >> 32) == fkey(s) && (uint32_t)(x / rows_per_qblk) == ~(uint32_t)ck;
+            }
+            if (cand) atomicMin(owner + j, x);
+            const float rs = reported(s, a.neg_out);
+            match_j[x] = cand ? j : -1;
+            match_s[x] = rs;
+            if (nn12) { nn12[x] = j; s12[x] = rs; }
+        }
     }
 }
 
@@ -595,12 +621,21 @@ __global__ void __launch_bounds__(OUT_NT) frm_output_kernel(FrmState st, int kca
 
 // ---------------------------------------------------------------------------
 // Ordered compaction of a dense match array (j >= 0 marks a pair) into sorted
-// (i, j, score) lists: per-block counts, one scan per pair, scatter.
+// (i, j, score) lists: per-block counts, one scan per pair, scatter. With
+// column owners (the mutual check), entry i is kept only if it holds the claim
+// on its column (owner[j] == i): rows that lost their column to a lower row
+// drop out here.
 // ---------------------------------------------------------------------------
 constexpr int CB = 1024;   // entries per compaction block (256 threads x 4)
 
+__device__ __forceinline__ bool kept_entry(const int32_t *mj, const int32_t *owner, int i, int n) {
+    if (i >= n) return false;
+    const int j = mj[i];
+    return j >= 0 && (!owner || owner[j] == i);
+}
+
 __global__ void __launch_bounds__(256) compact_count_kernel(const int32_t *match_j, long long n_bs, int n,
-                                                            int32_t *blockcnt, int nblk) {
+                                                            int32_t *blockcnt, int nblk, const int32_t *owner) {
     const int pair = blockIdx.y;
     const int32_t *mj = match_j + pair * n_bs;
     int c = 0;
@@ -608,7 +643,7 @@ __global__ void __launch_bounds__(256) compact_count_kernel(const int32_t *match
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int i = base + t * 256 + threadIdx.x;
-        c += (i < n && mj[i] >= 0) ? 1 : 0;
+        c += kept_entry(mj, owner, i, n) ? 1 : 0;
     }
     __shared__ int red[4];
     for (int m = 32; m > 0; m >>= 1) c += __shfl_xor(c, m);
@@ -649,7 +684,8 @@ __global__ void __launch_bounds__(256) compact_scan_kernel(const int32_t *blockc
 __global__ void __launch_bounds__(256) compact_scatter_kernel(const int32_t *match_j, const float *match_s,
                                                               long long n_bs, int n, const int32_t *blockoff,
                                                               int nblk, int32_t *out_i, int32_t *out_j,
-                                                              float *out_s, long long out_bs, int capacity) {
+                                                              float *out_s, long long out_bs, int capacity,
+                                                              const int32_t *owner) {
     const int pair = blockIdx.y;
     const int32_t *mj = match_j + pair * n_bs;
     const float *ms = match_s + pair * n_bs;
@@ -658,7 +694,7 @@ __global__ void __launch_bounds__(256) compact_scatter_kernel(const int32_t *mat
     int off = blockoff[pair * nblk + blockIdx.x];
     for (int t = 0; t < 4; ++t) {
         const int i = blockIdx.x * CB + t * 256 + threadIdx.x;
-        const bool valid = i < n && mj[i] >= 0;
+        const bool valid = kept_entry(mj, owner, i, n);
         const uint64_t ball = __ballot(valid);
         if (lane == 0) wcnt[w] = __popcll(ball);
         __syncthreads();
