@@ -128,6 +128,20 @@ def test_frm_different_image_sizes(ddm):
               j.cpu().numpy(), s.cpu().numpy(), oracle.seed_grid(30, 41, 3), 10)
 
 
+def test_frm_grouped_tasks_with_empty_slots(ddm):
+    """Sweep tasks that group several 768-row sub-blocks hand their (sub-block, query slot) units out through a
+    counter: 316x352 at stride 4 gives 6952 = 9 x 768 + 40 seeds against the 64 reference chunks of a 512x384
+    map, so the first sweep groups two sub-blocks per task and the last task's second sub-block (three 16-row
+    tiles) leaves five of its eight slots empty."""
+    D1 = synth.random_map(316, 352, 24, synth.F16, 61)
+    D2 = synth.random_map(512, 384, 24, synth.F16, 62)
+    i, j, s, st = ddm.frm_match(dev(D1, synth.F16), dev(D2, synth.F16), 4, 3, return_state=True)
+    seeds = oracle.seed_grid(316, 352, 4)
+    assert len(seeds) == 6952
+    check_frm(dec(D1, synth.F16), dec(D2, synth.F16), st["state"].cpu().numpy(), i.cpu().numpy(),
+              j.cpu().numpy(), s.cpu().numpy(), seeds, 3, query_counts=st["query_counts"].cpu().numpy())
+
+
 def test_frm_identity(ddm):
     p = synth.make_pair(64, 48, 24, synth.F16, 41, sigma=0.0, shift=(0, 0))
     i, j, s, st = ddm.frm_match(dev(p.D1, synth.F16), dev(p.D2, synth.F16), 4, 10, return_state=True)
